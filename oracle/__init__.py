@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for Parallax decode attention (test infrastructure only:
+imported by tests, the smoke check and the bench's CPU-baseline leg, never by
+the product path)."""
+from .parallax_oracle import (probe, softmax_weights, weighted_means, kv_covariance,
+                              decode_head, decode, decode_heads, kv_head_of)
+
+__all__ = ["probe", "softmax_weights", "weighted_means", "kv_covariance",
+           "decode_head", "decode", "decode_heads", "kv_head_of"]
