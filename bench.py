@@ -1,0 +1,255 @@
+"""Parallax decode benchmark on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the probe
+rho = W_R x followed by the decode (split-K pass + merge) for every sequence.
+The default workload is the mid-context GQA decode (B=16, Hq=16, Hkv=8, d=128,
+ctx=4096, d_model=2048, bf16 cache). Inputs are resident in HBM before timing;
+several independently seeded input sets are rotated so that every step reads
+its K/V cold (their total exceeds the last-level cache).
+
+Output: one JSON line (metric, value = decode tokens/s, ms_per_step, roofline
+of the dominant kernel, CPU oracle baseline, ...).
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload 2]
+                    [--sets 3] [--no-cpu-baseline] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Parallax decode tokens/s and HBM GB/s (% of peak) over batch×context sweep"
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak, GB/s
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SRC = os.path.join(ROOT, "parallax_covariance_corrected_amd", "csrc", "decode_mfma.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per decode launch from the committed rocprofv3 PMC summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, f"decode_mfma_{workload_name}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\s*(\{.*?\})\s*```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def upload_set(s, device="cuda"):
+    import torch
+    from parallax_covariance_corrected_amd.workloads import padded_cache
+    return dict(x=s.x.to(device), W_R=s.W_R.to(device), q=s.q.to(device),
+                seq_lens=s.seq_lens.to(device),
+                K=padded_cache(s.K, s.max_ctx, 0.0, device=device),
+                V=padded_cache(s.V, s.max_ctx, 0.0, device=device),
+                rho=torch.empty((s.wl.B, s.wl.Hq, s.wl.d), dtype=torch.float32, device=device),
+                out=torch.empty((s.wl.B, s.wl.Hq, s.wl.d), dtype=s.q.dtype, device=device))
+
+
+def step(pb, wl, d):
+    pb.probe(d["W_R"], d["x"], wl.Hq, wl.d, out=d["rho"])
+    pb.decode(d["q"], d["rho"], d["K"], d["V"], d["seq_lens"], out=d["out"])
+
+
+def cpu_baseline(s, budget_s: float = 12.0):
+    """The fp64 oracle on the host over a bounded sample of (sequence, head)
+    pairs of the same workload; tokens/s scaled to whole sequences."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    wl = s.wl
+    t0 = time.perf_counter()
+    rho = oracle.probe(s.W_R, s.x, wl.Hq, wl.d)
+    t_probe = time.perf_counter() - t0
+    q = s.q.float().numpy().astype(np.float64)
+    lens = s.seq_lens.tolist()
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.Hq)]
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in pairs:
+        oracle.decode_heads(q, rho, s.K, s.V, lens, wl.Hkv, [(b, h)])
+        done += 1
+        if time.perf_counter() - t0 > budget_s and done >= 4:
+            break
+    t_dec = time.perf_counter() - t0
+    # seconds for one full step = probe + all B*Hq heads at the measured per-head rate
+    step_s = t_probe + t_dec * (wl.B * wl.Hq) / done
+    return {"value": wl.B / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle probe for all {wl.B} sequences + decode of {done} of "
+                      f"{wl.B * wl.Hq} (sequence, head) pairs in {t_dec:.1f} s, "
+                      f"scaled to the full step"}
+
+
+def run_workload(args, wl_id: int, emit: bool = True):
+    import torch
+    from parallax_covariance_corrected_amd import binding as pb
+    from parallax_covariance_corrected_amd.workloads import WORKLOADS, make_inputs, algorithmic_bytes
+
+    wl = WORKLOADS[wl_id]
+    print(f"# bench: generating {args.sets} input sets for {wl.name}", file=sys.stderr, flush=True)
+    sets_host = [make_inputs(wl, seed) for seed in range(args.sets)]
+    dev_sets = [upload_set(s) for s in sets_host]
+    torch.cuda.synchronize()
+    tokens = [s.total_tokens() for s in sets_host]
+    chunk, splits, kernel = pb.decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.capacity,
+                                           pb.BF16 if wl.dtype == "bf16" else pb.F32)
+
+    for i in range(args.warmup):
+        step(pb, wl, dev_sets[i % len(dev_sets)])
+    torch.cuda.synchronize()
+    print(f"# bench: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    pb.profile_reset()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with pb.options(profile=1):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            step(pb, wl, dev_sets[i % len(dev_sets)])
+        ev1.record(stream)
+        torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    dec_ms, dec_n = pb.profile_read(pb.KERNEL_DECODE)
+    mrg_ms, mrg_n = pb.profile_read(pb.KERNEL_MERGE)
+    prb_ms, prb_n = pb.profile_read(pb.KERNEL_PROBE)
+    print(f"# bench: timed {args.steps} steps in {total_ms:.3f} ms", file=sys.stderr, flush=True)
+
+    ms_step = total_ms / args.steps
+    # algorithmic bytes, averaged over the rotated sets
+    ab = [algorithmic_bytes(wl, t) for t in tokens]
+    step_bytes = sum(a["total"] for a in ab) / len(ab) + wl.Hq * wl.d * wl.d_model * 2
+    dec_bytes = sum(a["decode_read"] for a in ab) / len(ab)
+    dec_avg_ms = dec_ms / max(dec_n, 1)
+    achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name) if wl_id == 2 else None
+    rec = {
+        "metric": METRIC,
+        "value": round(wl.B / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d,
+                   "ctx": wl.ctx, "max_ctx": wl.capacity, "d_model": wl.d_model,
+                   "kv_dtype": wl.dtype, "input_sets_rotated": args.sets,
+                   "plan": {"chunk": chunk, "splits": splits, "kernel": kernel}},
+        "hbm_gbps_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "pct_peak_step": round(100 * step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "decode_mfma_kernel (split-K pass)",
+                     "bytes_per_launch": int(dec_bytes),
+                     "avg_launch_us": round(dec_avg_ms * 1e3, 3),
+                     "merge_avg_us": round(mrg_ms / max(mrg_n, 1) * 1e3, 3),
+                     "probe_avg_us": round(prb_ms / max(prb_n, 1) * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if args.cpu_baseline:
+        print("# bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(sets_host[0])
+    if emit:
+        print(json.dumps(rec), flush=True)
+    return rec
+
+
+def run_sweep(args):
+    """Batch x context sweep at Hq=16, Hkv=8, d=128 bf16 (decode only, rotated
+    K/V so that every rep reads cold data); one JSON line per point."""
+    import torch
+    from parallax_covariance_corrected_amd import binding as pb
+    from parallax_covariance_corrected_amd.workloads import sweep_points
+
+    dev = "cuda"
+    max_bytes = args.sweep_max_gib << 30
+    for (B, ctx) in sweep_points(max_bytes // 2 if args.sweep_max_gib else 64 << 30):
+        kv = 2 * B * ctx * 8 * 128 * 2
+        nsets = max(1, min(3, (768 << 20) // kv + 1))
+        g = torch.Generator(device=dev).manual_seed(B * 100003 + ctx)
+        sets = []
+        for _ in range(nsets):
+            K = torch.randn((B, 8, ctx, 128), generator=g, device=dev).to(torch.bfloat16)
+            V = torch.randn((B, 8, ctx, 128), generator=g, device=dev).to(torch.bfloat16)
+            sets.append((K, V))
+        q = torch.randn((B, 16, 128), generator=g, device=dev).to(torch.bfloat16)
+        rho = torch.randn((B, 16, 128), generator=g, device=dev) * 0.1
+        lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+        out = torch.empty((B, 16, 128), dtype=torch.bfloat16, device=dev)
+        for i in range(5):
+            K, V = sets[i % nsets]
+            pb.decode(q, rho, K, V, lens, out=out)
+        torch.cuda.synchronize()
+        reps = 30
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            K, V = sets[i % nsets]
+            pb.decode(q, rho, K, V, lens, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        byts = kv + B * 16 * 128 * (2 + 4 + 2) + B * 4
+        print(json.dumps({"sweep": True, "B": B, "ctx": ctx, "us_per_step": round(us, 2),
+                          "tokens_per_s": round(B / (us * 1e-6), 1),
+                          "gbps": round(byts / (us * 1e-6) / 1e9, 1),
+                          "pct_peak": round(100 * byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)}),
+              flush=True)
+        del sets, q, rho, lens, out
+        torch.cuda.empty_cache()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--sweep-max-gib", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the Parallax decode path here is built and "
+              "measured on a single MI355X (multi-GPU sharding is a design note, not a run).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.sweep:
+        run_sweep(args)
+        return
+    run_workload(args, args.workload)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * parallax.h — C ABI of libparallax.so: Parallax decode attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Parallax keeps softmax attention and subtracts a learned covariance
+ * correction: the output for query i is softmax attention minus the
+ * softmax-weighted KV covariance multiplied by a probe rho_i = W_R x_i, where
+ * W_R is a learned projection of the layer input x_i; W_R = 0 gives plain
+ * softmax attention exactly (zubnet.ai (pt), "Parallax mantém softmax ...",
+ * second paragraph; zubnet.ai (fr), "Parallax garde softmax ...", second
+ * paragraph; encorp.ai (de), sections "Parallax behält Softmax bei" and "Warum
+ * das Entfernen des konjugierten Gradienten-Solvers ..."). The setting is
+ * decoding with a KV cache: one query token per sequence (same paragraph:
+ * the method still needs a KV cache and is not linear-complexity attention).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller. The library
+ *   never frees caller memory and keeps no pointer after a call returns.
+ * - Calls only enqueue work on `stream` (0 = the null stream) and return; the
+ *   results are valid once the caller synchronises that stream.
+ * - Arguments are checked on the host before any HIP call. On failure the call
+ *   returns a non-zero parallax_status, enqueues nothing and leaves a message
+ *   in parallax_last_error(). No C++ exception crosses this ABI.
+ * - All tensors are dense, row-major (last index fastest), 16-byte aligned.
+ * - dtype selects the storage type (see parallax_dtype). rho is always fp32
+ *   and all accumulation is fp32.
+ * - Calls are thread-safe; calls that share output buffers must be ordered by
+ *   the caller.
+ */
+#ifndef PARALLAX_H_
+#define PARALLAX_H_
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PARALLAX_OK = 0,
+  PARALLAX_ERR_INVALID_ARG = 1,   /* bad size, null or misaligned pointer, Hq % Hkv != 0 */
+  PARALLAX_ERR_UNSUPPORTED = 2,   /* valid but unsupported: d not in {64, 128}, unknown dtype */
+  PARALLAX_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed */
+  PARALLAX_ERR_NO_MEMORY = 4      /* the split-K workspace could not be allocated */
+} parallax_status;
+
+typedef enum {
+  PARALLAX_F32 = 0,          /* x, W_R, q, K, V, out: fp32                              */
+  PARALLAX_BF16 = 1,         /* x, W_R, q, K, V, out: bf16 (out rounded to nearest even) */
+  PARALLAX_BF16_F32OUT = 2   /* x, W_R, q, K, V: bf16; out: fp32 (same arithmetic as
+                                PARALLAX_BF16 up to the final rounding)                  */
+} parallax_dtype;
+
+/*
+ * parallax_probe — the layer-input probe rho = W_R x (zubnet.ai (pt),
+ * "Parallax mantém softmax ...", second paragraph: the learned projection W_R
+ * probes the KV covariance directly from the layer input).
+ *
+ *   W_R : [Hq*d, d_model], dtype storage (bf16 for both bf16 dtypes)
+ *   x   : [B, d_model],    dtype storage
+ *   rho : [B, Hq, d] fp32 output; rho[b][h][i] = sum_c W_R[h*d + i][c] * x[b][c]
+ *
+ * Row h*d + i of W_R produces component i of query head h's probe (one probe
+ * per query head). Requires B >= 1, Hq >= 1, d in {64, 128}, d_model >= 1, and
+ * d_model % 8 == 0 for the bf16 dtypes.
+ */
+int parallax_probe(const void* W_R, const void* x, float* rho,
+                   int B, int Hq, int d, int d_model, int dtype, hipStream_t stream);
+
+/*
+ * parallax_decode — one decode step of Parallax attention (zubnet.ai (pt),
+ * second paragraph: softmax attention minus the KV covariance times the probe;
+ * both branches read the same KV stream — same paragraph and encorp.ai (de),
+ * section "Wie Parallax die Hardware-Geschichte auf Hopper-GPUs verändert").
+ *
+ * For every sequence b and query head h, with g = h / (Hq / Hkv) and
+ * n = seq_lens[b], over cached tokens j = 0 .. n-1:
+ *   s_j  = q[b][h] . K[b][g][j] / sqrt(d),   w = softmax(s)
+ *   kbar = sum_j w_j K[b][g][j],   vbar = sum_j w_j V[b][g][j]
+ *   C    = sum_j w_j (V[b][g][j] - vbar)(K[b][g][j] - kbar)^T      (d x d)
+ *   out[b][h] = vbar - C rho[b][h]
+ * computed in one pass as out = A/l - (P/l - (A/l)(S/l)) from the running sums
+ * l = sum e_j, S = sum e_j p_j, A = sum e_j v_j, P = sum e_j p_j v_j with
+ * e_j = exp(s_j - max s) and p_j = K[b][g][j] . rho[b][h].
+ *
+ *   q        : [B, Hq, d]               dtype storage (bf16 for both bf16 dtypes)
+ *   rho      : [B, Hq, d]               fp32 (from parallax_probe)
+ *   k_cache  : [B, Hkv, max_ctx, d]     dtype storage; rows j >= seq_lens[b] are never read
+ *   v_cache  : [B, Hkv, max_ctx, d]     same layout as k_cache
+ *   seq_lens : [B] int32, device memory; 0 <= seq_lens[b] <= max_ctx
+ *   out      : [B, Hq, d]               fp32 or bf16 per dtype
+ *
+ * Requires B, Hq, Hkv, max_ctx >= 1, Hq % Hkv == 0, d in {64, 128}. A sequence
+ * with seq_lens[b] == 0 gets out = 0 (a convention). seq_lens[b] > max_ctx is
+ * clamped to max_ctx on the device (memory safety; a caller error). Long
+ * sequences are split into chunks processed in parallel and merged by their
+ * running maxima; the split-K workspace is allocated stream-ordered on
+ * `stream` (hipMallocAsync / hipFreeAsync) and released by the same stream.
+ */
+int parallax_decode(const void* q, const float* rho, const void* k_cache,
+                    const void* v_cache, const int* seq_lens, void* out,
+                    int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
+                    hipStream_t stream);
+
+/* Message of the last non-OK status returned on the calling thread ("" if none). */
+const char* parallax_last_error(void);
+
+/*
+ * parallax_decode_plan — the launch plan parallax_decode would use (for tests
+ * and measurement). Writes the chunk length in keys, the number of splits per
+ * (sequence, KV head) and the decode kernel (1 = generic vector-ALU kernel,
+ * 2 = matrix-core kernel). Same argument checks as parallax_decode.
+ */
+int parallax_decode_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
+                         int* chunk, int* splits, int* kernel);
+
+/*
+ * Process-wide tuning options (for tests and measurement). Not to be changed
+ * while other threads call the library.
+ *   PARALLAX_OPT_CHUNK   : 0 = automatic, else keys per split (multiple of 128)
+ *   PARALLAX_OPT_KERNEL  : 0 = automatic, 1 = force the generic kernel,
+ *                          2 = force the matrix-core kernel (where supported)
+ *   PARALLAX_OPT_PROFILE : 1 = record HIP events around every kernel launch
+ */
+typedef enum {
+  PARALLAX_OPT_CHUNK = 1,
+  PARALLAX_OPT_KERNEL = 2,
+  PARALLAX_OPT_PROFILE = 3
+} parallax_option;
+
+int parallax_set_option(int option, int value);
+int parallax_get_option(int option, int* value);
+
+/*
+ * Kernel timing through HIP events recorded on the launch stream when
+ * PARALLAX_OPT_PROFILE is 1. kernel: 0 = probe, 1 = decode (split-K pass),
+ * 2 = merge. parallax_profile_read waits for the recorded events and returns
+ * the summed duration (ms) and the number of launches since the last reset.
+ */
+int parallax_profile_read(int kernel, double* total_ms, long long* launches);
+int parallax_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif  /* PARALLAX_H_ */

@@ -1,0 +1,295 @@
+// Host side of the libparallax C ABI (declared in include/parallax.h):
+// argument checks, the split-K plan, the stream-ordered workspace, kernel
+// launches, error reporting and optional per-kernel event timing.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/parallax.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PARALLAX_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ---------------------------------------------------------------- options
+int g_opt_chunk = 0;
+int g_opt_kernel = 0;
+int g_opt_profile = 0;
+
+// ---------------------------------------------------------------- profiling
+struct Timing {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+  double total_ms = 0.0;
+  long long launches = 0;
+};
+std::mutex g_prof_mu;
+Timing g_prof[3];
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records an event before a launch and, via finish(), after it.
+struct KernelTimer {
+  int kind;
+  hipStream_t stream;
+  hipEvent_t start = nullptr;
+  KernelTimer(int k, hipStream_t s) : kind(k), stream(s) {
+    if (!g_opt_profile) return;
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    start = take_event();
+    if (start && hipEventRecord(start, stream) != hipSuccess) start = nullptr;
+  }
+  void finish() {
+    if (!start) return;
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    hipEvent_t stop = take_event();
+    if (stop && hipEventRecord(stop, stream) == hipSuccess) {
+      g_prof[kind].pending.emplace_back(start, stop);
+    } else {
+      g_event_pool.push_back(start);
+      if (stop) g_event_pool.push_back(stop);
+    }
+    start = nullptr;
+  }
+};
+
+// ---------------------------------------------------------------- planning
+struct Plan {
+  int chunk;
+  int splits;
+  int kernel;   // 1 generic, 2 matrix-core
+};
+
+int esize(int dtype) { return dtype == PARALLAX_F32 ? 4 : 2; }
+
+int check_decode_shape(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
+  if (dtype != PARALLAX_F32 && dtype != PARALLAX_BF16 && dtype != PARALLAX_BF16_F32OUT)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
+  if (B < 1 || Hq < 1 || Hkv < 1 || max_ctx < 1)
+    return fail(PARALLAX_ERR_INVALID_ARG, "B, Hq, Hkv and max_ctx must be >= 1");
+  if (Hq % Hkv != 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+  if (d != 64 && d != 128)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "head dim d must be 64 or 128");
+  // Buffer offsets inside one (sequence, KV head) stream are 32-bit.
+  if ((long long)max_ctx * d * esize(dtype) + 256LL * d * esize(dtype) >= (1LL << 31))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "max_ctx too large for one KV stream (2 GiB)");
+  if ((long long)B * Hq > (1LL << 30))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "B * Hq too large");
+  return PARALLAX_OK;
+}
+
+Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
+  Plan p;
+  const int G = Hq / Hkv;
+  p.kernel = (dtype == PARALLAX_F32) ? 1 : 2;
+  if (g_opt_kernel == 1) p.kernel = 1;
+  if (g_opt_kernel == 2 && dtype != PARALLAX_F32 && parallax::decode_mfma_supported(d, G)) p.kernel = 2;
+  int chunk = g_opt_chunk;
+  if (chunk <= 0) {
+    // Enough workgroups to keep every CU busy (~2048), chunks of 128..2048 keys.
+    const long long units = (long long)B * Hkv;
+    const long long want = units >= 2048 ? 1 : (2048 + units - 1) / units;
+    long long c = (max_ctx + want - 1) / want;
+    c = (c + 127) / 128 * 128;
+    if (c < 128) c = 128;
+    if (c > 2048) c = 2048;
+    chunk = (int)c;
+  }
+  p.chunk = chunk;
+  p.splits = (max_ctx + chunk - 1) / chunk;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* parallax_last_error(void) { return g_last_error.c_str(); }
+
+int parallax_set_option(int option, int value) {
+  switch (option) {
+    case PARALLAX_OPT_CHUNK:
+      if (value < 0 || value % 128 != 0)
+        return fail(PARALLAX_ERR_INVALID_ARG, "chunk must be 0 or a positive multiple of 128");
+      g_opt_chunk = value;
+      return PARALLAX_OK;
+    case PARALLAX_OPT_KERNEL:
+      if (value < 0 || value > 2) return fail(PARALLAX_ERR_INVALID_ARG, "kernel must be 0, 1 or 2");
+      g_opt_kernel = value;
+      return PARALLAX_OK;
+    case PARALLAX_OPT_PROFILE:
+      if (value != 0 && value != 1) return fail(PARALLAX_ERR_INVALID_ARG, "profile must be 0 or 1");
+      g_opt_profile = value;
+      return PARALLAX_OK;
+    default:
+      return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
+  }
+}
+
+int parallax_get_option(int option, int* value) {
+  if (!value) return fail(PARALLAX_ERR_INVALID_ARG, "value is null");
+  switch (option) {
+    case PARALLAX_OPT_CHUNK: *value = g_opt_chunk; return PARALLAX_OK;
+    case PARALLAX_OPT_KERNEL: *value = g_opt_kernel; return PARALLAX_OK;
+    case PARALLAX_OPT_PROFILE: *value = g_opt_profile; return PARALLAX_OK;
+    default: return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
+  }
+}
+
+int parallax_profile_reset(void) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (auto& t : g_prof) {
+    for (auto& pr : t.pending) {
+      (void)hipEventSynchronize(pr.second);
+      g_event_pool.push_back(pr.first);
+      g_event_pool.push_back(pr.second);
+    }
+    t.pending.clear();
+    t.total_ms = 0.0;
+    t.launches = 0;
+  }
+  return PARALLAX_OK;
+}
+
+int parallax_profile_read(int kernel, double* total_ms, long long* launches) {
+  if (kernel < 0 || kernel > 2) return fail(PARALLAX_ERR_INVALID_ARG, "kernel must be 0, 1 or 2");
+  if (!total_ms || !launches) return fail(PARALLAX_ERR_INVALID_ARG, "null output pointer");
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  Timing& t = g_prof[kernel];
+  for (auto& pr : t.pending) {
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    t.total_ms += ms;
+    t.launches += 1;
+    g_event_pool.push_back(pr.first);
+    g_event_pool.push_back(pr.second);
+  }
+  t.pending.clear();
+  *total_ms = t.total_ms;
+  *launches = t.launches;
+  return PARALLAX_OK;
+}
+
+int parallax_probe(const void* W_R, const void* x, float* rho, int B, int Hq, int d,
+                   int d_model, int dtype, hipStream_t stream) {
+  if (dtype != PARALLAX_F32 && dtype != PARALLAX_BF16 && dtype != PARALLAX_BF16_F32OUT)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
+  if (!W_R || !x || !rho) return fail(PARALLAX_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(W_R, 16) || !aligned(x, 16) || !aligned(rho, 16))
+    return fail(PARALLAX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (B < 1 || Hq < 1 || d_model < 1)
+    return fail(PARALLAX_ERR_INVALID_ARG, "B, Hq and d_model must be >= 1");
+  if (d != 64 && d != 128) return fail(PARALLAX_ERR_UNSUPPORTED, "head dim d must be 64 or 128");
+  const bool f32 = dtype == PARALLAX_F32;
+  if (!f32 && d_model % 8 != 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "d_model must be a multiple of 8 for bf16");
+  if ((long long)d_model * 2 * 64 >= (1LL << 30) || (long long)Hq * d > (1LL << 28) ||
+      (long long)B > (1LL << 22))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "probe size out of range");
+  KernelTimer tm(0, stream);
+  hipError_t e = parallax::launch_probe(W_R, x, rho, B, Hq * d, d_model, f32 ? 1 : 0, stream);
+  tm.finish();
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return PARALLAX_OK;
+}
+
+int parallax_decode_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype, int* chunk,
+                         int* splits, int* kernel) {
+  int rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
+  if (rc != PARALLAX_OK) return rc;
+  if (!chunk || !splits || !kernel) return fail(PARALLAX_ERR_INVALID_ARG, "null output pointer");
+  const Plan p = make_plan(B, Hq, Hkv, d, max_ctx, dtype);
+  *chunk = p.chunk;
+  *splits = p.splits;
+  *kernel = p.kernel;
+  return PARALLAX_OK;
+}
+
+int parallax_decode(const void* q, const float* rho, const void* k_cache, const void* v_cache,
+                    const int* seq_lens, void* out, int B, int Hq, int Hkv, int d, int max_ctx,
+                    int dtype, hipStream_t stream) {
+  int rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
+  if (rc != PARALLAX_OK) return rc;
+  if (!q || !rho || !k_cache || !v_cache || !seq_lens || !out)
+    return fail(PARALLAX_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(q, 16) || !aligned(rho, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, 16) || !aligned(seq_lens, 4))
+    return fail(PARALLAX_ERR_INVALID_ARG, "pointers must be 16-byte aligned (seq_lens 4-byte)");
+
+  const Plan p = make_plan(B, Hq, Hkv, d, max_ctx, dtype);
+  parallax::DecodeArgs a;
+  a.q = q;
+  a.rho = rho;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.ml = nullptr;
+  a.ap = nullptr;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.max_ctx = max_ctx;
+  a.chunk = p.chunk;
+  a.splits = p.splits;
+  a.out_f32 = (dtype == PARALLAX_BF16) ? 0 : 1;
+  a.scale_log2 = parallax::kLog2e / sqrtf((float)d);
+
+  void* ws = nullptr;
+  if (p.splits > 1) {
+    const size_t states = (size_t)B * Hq * p.splits;
+    const size_t bytes = states * sizeof(float4) + states * 2 * d * sizeof(float);
+    hipError_t e = hipMallocAsync(&ws, bytes, stream);
+    if (e != hipSuccess || !ws) return fail(PARALLAX_ERR_NO_MEMORY, "split-K workspace allocation failed");
+    a.ml = (float4*)ws;
+    a.ap = (float*)((char*)ws + states * sizeof(float4));
+  }
+
+  hipError_t e;
+  {
+    KernelTimer tm(1, stream);
+    e = (p.kernel == 2) ? parallax::launch_decode_mfma(a, d, stream)
+                        : parallax::launch_decode_generic(a, d, dtype == PARALLAX_F32 ? 1 : 0, stream);
+    tm.finish();
+  }
+  if (e == hipSuccess && p.splits > 1) {
+    KernelTimer tm(2, stream);
+    e = parallax::launch_merge(a, d, stream);
+    tm.finish();
+  }
+  if (ws) {
+    hipError_t f = hipFreeAsync(ws, stream);
+    if (e == hipSuccess && f != hipSuccess) e = f;
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return PARALLAX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Shared device helpers and internal launcher declarations for libparallax.
+// gfx950 (CDNA4) only: 64-lane wavefronts, bf16 matrix cores, raw buffer loads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace parallax {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+
+// bf16 storage is handled as raw 16-bit patterns; the value of a bf16 is the
+// fp32 with the same top 16 bits.
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((unsigned)b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  unsigned lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+// Raw buffer resource over [base, base + bytes): loads at byte offsets past
+// `bytes` return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
+// exp2 on the hardware transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Scale factor that moves a running sum from reference max m_old to m_new
+// (log2 domain); an empty state (m_old = -inf) contributes nothing.
+__device__ __forceinline__ float rescale(float m_old, float m_new) {
+  return m_old == kNegInf ? 0.f : fast_exp2(m_old - m_new);
+}
+
+// Final epilogue: out = A/l - (P/l - (A/l)(S/l)); l == 0 (no keys) gives 0.
+__device__ __forceinline__ float parallax_out(float A, float P, float l, float S) {
+  if (!(l > 0.f)) return 0.f;
+  float inv = 1.f / l;
+  float vbar = A * inv;
+  return vbar - (P * inv - vbar * (S * inv));
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(T* p, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
+  *p = f32_to_bf16_rne(v);
+}
+
+// Split-K partial state of one (sequence, query head, split), fp32:
+//   ml[(b*Hq + h)*splits + s] = {m (log2 domain), l, S, 0}
+//   ap[((b*Hq + h)*splits + s)*2*d + {0: A, d: P} + i]
+struct DecodeArgs {
+  const void* q;
+  const float* rho;
+  const void* k;
+  const void* v;
+  const int* seq_lens;
+  void* out;
+  float4* ml;
+  float* ap;
+  int B, Hq, Hkv, max_ctx;
+  int chunk;       // keys per split
+  int splits;      // splits per (sequence, KV head); 1 => write out directly
+  int out_f32;     // 1: out is fp32, 0: bf16
+  float scale_log2;  // log2(e) / sqrt(d)
+};
+
+// Internal launchers (one translation unit each). Return hipError_t.
+hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s);
+bool decode_mfma_supported(int d, int G);
+hipError_t launch_merge(const DecodeArgs& a, int d, hipStream_t s);
+hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, int K,
+                        int f32_inputs, hipStream_t s);
+
+}  // namespace parallax

@@ -1,0 +1,380 @@
+// Matrix-core Parallax decode kernel for gfx950 (bf16 K/V cache, d in {64, 128}).
+//
+// What it computes (zubnet.ai (pt), "Parallax mantém softmax ...", second
+// paragraph): per query head, softmax attention minus the softmax-weighted KV
+// covariance times the probe rho, in the one-pass form
+//   out = A/l - (P/l - (A/l)(S/l)),  l = sum e, S = sum e p, A = sum e v,
+//   P = sum e p v,  e = exp(s - m),  s = q.k/sqrt(d),  p = k.rho,
+// with both branches fed by one read of each K/V row (same paragraph: the KV
+// stream is shared, which is what doubles the arithmetic intensity).
+//
+// Work decomposition: one workgroup (4 waves) per (sequence, KV head, head
+// block, split of `chunk` keys). A wave takes 32 keys per step (two 16-key
+// tiles), steps strided by 128 keys, with the next step's K/V prefetched into
+// registers. K/V rows are read with raw buffer loads whose range ends at the
+// last key of the split, so the ragged tail reads zeros without touching
+// memory (and never reads past seq_lens).
+//
+// Per 16-key tile:
+//  * scores and probes: one bf16 16x16x32 MFMA product  K_tile (16 keys x 32
+//    dims) . X^T (32 dims x 16 columns)  per 32 dims, where the columns of X are
+//    q of each head (exact: bf16 x bf16 products are exact in fp32) and rho of
+//    each head split as rho_hi + rho_lo (two bf16 operands accumulated into the
+//    same fp32 result), so rho keeps ~16 significant bits.
+//    Lane l receives 4 keys (4*(l/16) + r) of one column (l % 16).
+//  * online softmax with a lazy rescale: the running max moves only when a
+//    tile max exceeds it by more than 8 (log2 units), so e <= 2^8 between
+//    rescales and almost every tile skips the rescale.
+//  * weights: e for the score columns, e*p for the probe columns, moved next to
+//    each other with DPP lane moves inside 4- or 16-lane rows.
+//  * weighted value sums: fp32 4x4x1 MFMA blocks (16 blocks per instruction):
+//    A operand = the weight rows (e_h, e_h p_h) of one key, B operand = 4
+//    value dims of that key, so weights stay fp32 (a bf16 weight would cost
+//    about 1e-3 relative error) and V needs no transpose: each lane's 16-byte
+//    V load supplies 8 consecutive dims.
+// Wave states are merged in LDS; with one split the workgroup writes out,
+// otherwise it writes its partial (m, l, S, A, P) for the merge kernel.
+#include <type_traits>
+
+#include "common.h"
+
+namespace parallax {
+namespace {
+
+constexpr float kRescaleThreshold = 8.0f;   // log2 units
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+constexpr int kDppRowShl8 = 0x108;   // lane i reads lane i+8 of its 16-lane row
+constexpr int kDppRowShr8 = 0x118;   // lane i reads lane i-8 of its 16-lane row
+
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+template <int GH>
+struct Layout {
+  // Weight row r of MFMA set `set` -> query head of the block (-1: unused row)
+  // and whether it accumulates A (e v) or P (e p v).
+  static constexpr int NSET = GH <= 2 ? 1 : 2;
+  __device__ static constexpr int head(int set, int r) {
+    return GH <= 2 ? (r < GH ? r : (r < 2 * GH ? r - GH : -1)) : (r < GH ? r : -1);
+  }
+  __device__ static constexpr bool is_A(int set, int r) {
+    return GH <= 2 ? (r < GH) : (set == 0);
+  }
+};
+
+template <int D>
+struct KV {
+  static constexpr int NC = D / 32;    // 32-dim chunks of the score product
+  static constexpr int EPV = D / 16;   // value dims per lane
+  static constexpr int ROW = 2 * D;    // bytes per cache row
+  using VW = typename std::conditional<D == 128, u32x4, u32x2>::type;
+  struct Step {
+    u32x4 k[2][NC];
+    VW v[2][4];
+  };
+  __device__ static VW vload(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    if constexpr (D == 128) return buf_load16(r, off);
+    else return buf_load8(r, off);
+  }
+  __device__ static float velem(const VW& w, int t) {
+    return (t & 1) ? bf16_hi(w[t >> 1]) : bf16_lo(w[t >> 1]);
+  }
+};
+
+template <int D, int GH>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+  using L = Layout<GH>;
+  using C = KV<D>;
+  constexpr int NC = C::NC, EPV = C::EPV, ROW = C::ROW, NSET = L::NSET;
+
+  const int G = a.Hq / a.Hkv;
+  const int hblocks = G / GH;
+  int wg = blockIdx.x;
+  const int split = wg % a.splits; wg /= a.splits;
+  const int hb = wg % hblocks; wg /= hblocks;
+  const int kvh = wg % a.Hkv;
+  const int b = wg / a.Hkv;
+  const int n = min(max(a.seq_lens[b], 0), a.max_ctx);
+  const int c0 = split * a.chunk;
+  if (a.splits > 1 && c0 >= n) return;   // empty split: the merge never reads it
+  const int c1 = min(c0 + a.chunk, n);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4, quad = l16 >> 2, qi = lane & 3;
+  const int h0 = kvh * G + hb * GH;
+
+  // Column role of this lane in the score/probe product.
+  bool is_s, is_p;
+  int chead;
+  if constexpr (GH <= 2) {
+    is_s = qi < GH;
+    is_p = !is_s && qi < 2 * GH;
+    chead = is_s ? qi : qi - GH;
+  } else {
+    is_s = quad < 2 && qi < GH;
+    is_p = quad >= 2 && qi < GH;
+    chead = qi;
+  }
+
+  // B operands: column vector (q, or rho split hi + lo) at dims 32c + 8*grp + t.
+  bf16x8 bhi[NC], blo[NC];
+  {
+    const size_t bh = (size_t)b * a.Hq + h0 + chead;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+      const size_t off = bh * D + 32 * c + 8 * grp;
+      if (is_s) {
+        hi = *(const u32x4*)((const uint16_t*)a.q + off);
+      } else if (is_p) {
+        const float4 r0 = *(const float4*)(a.rho + off);
+        const float4 r1 = *(const float4*)(a.rho + off + 4);
+        const float r[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint16_t h_a = f32_to_bf16_rne(r[2 * w]), h_b = f32_to_bf16_rne(r[2 * w + 1]);
+          const uint16_t l_a = f32_to_bf16_rne(r[2 * w] - bf16_bits_to_f32(h_a));
+          const uint16_t l_b = f32_to_bf16_rne(r[2 * w + 1] - bf16_bits_to_f32(h_b));
+          hi[w] = (unsigned)h_a | ((unsigned)h_b << 16);
+          lo[w] = (unsigned)l_a | ((unsigned)l_b << 16);
+        }
+      }
+      bhi[c] = as_bf16x8(hi);
+      blo[c] = as_bf16x8(lo);
+    }
+  }
+
+  const size_t seq = ((size_t)b * a.Hkv + kvh) * (size_t)a.max_ctx;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc((const char*)a.k + seq * ROW, (unsigned)c1 * ROW);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const char*)a.v + seq * ROW, (unsigned)c1 * ROW);
+  const unsigned koff = l16 * ROW + 16 * grp;
+  const unsigned voff = 4 * grp * ROW + l16 * (ROW / 16);
+
+  auto load = [&](typename C::Step& st, int j) {
+    const unsigned base = (unsigned)j * ROW;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) st.k[u][c] = buf_load16(krs, base + u * 16 * ROW + koff + 64 * c);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) st.v[u][c] = C::vload(vrs, base + u * 16 * ROW + voff + c * ROW);
+  };
+
+  float m_run = kNegInf;      // running max (log2 domain), score lanes
+  float lsum = 0.f, ssum = 0.f;
+  f32x4 acc[NSET][EPV];
+#pragma unroll
+  for (int s = 0; s < NSET; ++s)
+#pragma unroll
+    for (int t = 0; t < EPV; ++t) acc[s][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const typename C::Step& st, int j) {
+    float val[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[u][c]), bhi[c], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[u][c]), blo[c], sacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) val[u][r] = sacc[r];
+    }
+    float x[2][4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = j + 16 * u + 4 * grp + r;
+        x[u][r] = (is_s && key < c1) ? val[u][r] * a.scale_log2 : kNegInf;
+        tmax = fmaxf(tmax, x[u][r]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const bool need = is_s && (tmax > m_run + kRescaleThreshold);
+    if (__any(need)) {
+      const float mnew = need ? tmax : m_run;
+      const float alpha = need ? rescale(m_run, mnew) : 1.f;
+      if (is_s) m_run = mnew;
+      float ah[GH];
+#pragma unroll
+      for (int h = 0; h < GH; ++h) ah[h] = readlane_f(alpha, h);
+#pragma unroll
+      for (int s = 0; s < NSET; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = L::head(s, r);
+          if (h < 0) continue;
+#pragma unroll
+          for (int t = 0; t < EPV; ++t) acc[s][t][r] *= ah[h];
+        }
+      float a0 = 1.f, a1 = 1.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (qi == r && L::head(0, r) >= 0) a0 = ah[L::head(0, r)];
+        if (NSET > 1 && qi == r && L::head(1, r) >= 0) a1 = ah[L::head(1, r)];
+      }
+      lsum *= a0;
+      ssum *= a1;
+    }
+    float w0[2][4], w1[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = is_s ? fast_exp2(x[u][r] - m_run) : 0.f;
+        if constexpr (GH <= 2) {
+          constexpr int kQuadPerm = GH == 2 ? 0x44 : 0x00;   // lane qi reads lane qi - GH
+          const float esrc = dpp<kQuadPerm>(e);
+          w0[u][r] = is_s ? e : (is_p ? esrc * val[u][r] : 0.f);
+          lsum += w0[u][r];
+        } else {
+          const float efrom = dpp<kDppRowShr8>(e);
+          const float ep = efrom * val[u][r];
+          const float epto = dpp<kDppRowShl8>(ep);
+          w0[u][r] = is_s ? e : (is_p ? efrom : 0.f);
+          w1[u][r] = is_s ? epto : (is_p ? ep : 0.f);
+          lsum += w0[u][r];
+          ssum += w1[u][r];
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int t = 0; t < EPV; ++t) {
+          const float vf = C::velem(st.v[u][c], t);
+          acc[0][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w0[u][c], vf, acc[0][t], 0, 0, 0);
+          if constexpr (NSET > 1)
+            acc[1][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w1[u][c], vf, acc[1][t], 0, 0, 0);
+        }
+      }
+  };
+
+  {
+    typename C::Step sa, sb;
+    int j = c0 + 32 * wave;
+    load(sa, j);
+    while (j < c1) {
+      load(sb, j + 128);
+      compute(sa, j);
+      j += 128;
+      if (j >= c1) break;
+      load(sa, j + 128);
+      compute(sb, j);
+      j += 128;
+    }
+  }
+
+  // Sum the four key slots (lane groups of 16) of this wave.
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if constexpr (NSET > 1) {
+    ssum += __shfl_xor(ssum, 16);
+    ssum += __shfl_xor(ssum, 32);
+  }
+#pragma unroll
+  for (int s = 0; s < NSET; ++s)
+#pragma unroll
+    for (int t = 0; t < EPV; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = acc[s][t][r];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[s][t][r] = v;
+      }
+
+  __shared__ float sA[4][GH][D], sP[4][GH][D], sM[4][GH], sL[4][GH], sS[4][GH];
+  if (grp == 0) {
+#pragma unroll
+    for (int s = 0; s < NSET; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = L::head(s, r);
+        if (h < 0) continue;
+#pragma unroll
+        for (int t = 0; t < EPV; ++t) {
+          if (L::is_A(s, r)) sA[wave][h][l16 * EPV + t] = acc[s][t][r];
+          else sP[wave][h][l16 * EPV + t] = acc[s][t][r];
+        }
+      }
+    if (lane < GH) sM[wave][lane] = m_run;
+    if constexpr (GH <= 2) {
+      if (lane < GH) sL[wave][lane] = lsum;
+      else if (lane < 2 * GH) sS[wave][lane - GH] = lsum;
+    } else {
+      if (lane < GH) { sL[wave][lane] = lsum; sS[wave][lane] = ssum; }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < GH * D; idx += 256) {
+    const int h = idx / D, i = idx % D;
+    float M = sM[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sM[w][h]);
+    float lt = 0.f, St = 0.f, At = 0.f, Pt = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float c = rescale(sM[w][h], M);
+      lt = fmaf(c, sL[w][h], lt); St = fmaf(c, sS[w][h], St);
+      At = fmaf(c, sA[w][h][i], At); Pt = fmaf(c, sP[w][h][i], Pt);
+    }
+    const size_t bh = (size_t)b * a.Hq + h0 + h;
+    if (a.splits == 1) {
+      const float o = parallax_out(At, Pt, lt, St);
+      if (a.out_f32) store_out<float>((float*)a.out + bh * D + i, o);
+      else store_out<uint16_t>((uint16_t*)a.out + bh * D + i, o);
+    } else {
+      const size_t ps = bh * a.splits + split;
+      a.ap[ps * 2 * D + i] = At;
+      a.ap[ps * 2 * D + D + i] = Pt;
+      if (i == 0) a.ml[ps] = make_float4(M, lt, St, 0.f);
+    }
+  }
+}
+
+int head_block(int G) {
+  if (G <= 4) return G;
+  if (G % 4 == 0) return 4;
+  if (G % 3 == 0) return 3;
+  if (G % 2 == 0) return 2;
+  return 1;
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  const int GH = head_block(G);
+  const size_t grid = (size_t)a.B * a.Hkv * (G / GH) * a.splits;
+  if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  switch (GH) {
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4>), dim3(grid), dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<D, 3>), dim3(grid), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<D, 2>), dim3(grid), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_mfma_kernel<D, 1>), dim3(grid), dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_mfma_supported(int d, int G) { return (d == 64 || d == 128) && G >= 1; }
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
+  return d == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
+}
+
+}  // namespace parallax

@@ -1,0 +1,134 @@
+// Probe rho = W_R x for every sequence and query head (zubnet.ai (pt),
+// "Parallax mantém softmax ...", second paragraph: rho_i = W_R x_i from the
+// layer input).
+//
+// As a matrix product: rho[B, N] = x[B, K] . W_R[N, K]^T with N = Hq*d and
+// K = d_model; both operands have K contiguous, which is exactly the operand
+// layout of the bf16 MFMA (8 consecutive K values per lane), so no transpose
+// or LDS staging of operands is needed. Products of bf16 values are exact in
+// fp32 and the accumulation is fp32.
+//
+// bf16 kernel: a workgroup (4 waves) owns a (16*MT rows) x (16*NT columns)
+// tile; its waves split K four ways (32-wide steps strided by 128) and reduce
+// through LDS in a fixed order. Rows past B read zeros (buffer range).
+// fp32 kernel: one thread per output, a plain dot product.
+#include "common.h"
+
+namespace parallax {
+namespace {
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+template <int MT, int NT>
+__global__ __launch_bounds__(256) void probe_mfma_kernel(const uint16_t* __restrict__ W,
+                                                         const uint16_t* __restrict__ x,
+                                                         float* __restrict__ rho, int B, int N,
+                                                         int K) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NT;
+  const int m0 = blockIdx.y * 16 * MT;
+  const unsigned rowb = (unsigned)K * 2;
+  // x rows m0.. (rows >= B read as zero), W rows n0..
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (size_t)m0 * K,
+                                              (unsigned)(min(B - m0, 16 * MT)) * rowb);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + (size_t)n0 * K,
+                                              (unsigned)(min(N - n0, 16 * NT)) * rowb);
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int jn = 0; jn < NT; ++jn) acc[i][jn] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+
+  for (int k0 = 32 * wave; k0 < K; k0 += 128) {
+    u32x4 xa[MT], wb[NT];
+    // K % 8 == 0, so an 8-wide group is entirely inside or past the row; a
+    // group past the row gets an offset beyond the buffer range and reads 0.
+    const unsigned koff = (k0 + 8 * grp < K) ? (unsigned)(k0 + 8 * grp) * 2 : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) xa[i] = buf_load16(xr, (unsigned)(16 * i + l16) * rowb + koff);
+#pragma unroll
+    for (int jn = 0; jn < NT; ++jn) wb[jn] = buf_load16(wr, (unsigned)(16 * jn + l16) * rowb + koff);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int jn = 0; jn < NT; ++jn)
+        acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[i]), as_bf16x8(wb[jn]),
+                                                              acc[i][jn], 0, 0, 0);
+  }
+
+  __shared__ f32x4 red[3][MT * NT][64];
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int jn = 0; jn < NT; ++jn) red[wave - 1][i * NT + jn][lane] = acc[i][jn];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int jn = 0; jn < NT; ++jn) {
+        f32x4 v = acc[i][jn];
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+          const f32x4 o = red[w][i * NT + jn][lane];
+          v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
+        }
+        const int col = n0 + 16 * jn + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + 16 * i + 4 * grp + r;
+          if (row < B && col < N) rho[(size_t)row * N + col] = v[r];
+        }
+      }
+  }
+}
+
+__global__ __launch_bounds__(256) void probe_f32_kernel(const float* __restrict__ W,
+                                                        const float* __restrict__ x,
+                                                        float* __restrict__ rho, int B, int N,
+                                                        int K) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)B * N) return;
+  const int row = (int)(idx / N), col = (int)(idx % N);
+  const float* w = W + (size_t)col * K;
+  const float* xr = x + (size_t)row * K;
+  float s = 0.f;
+  for (int k = 0; k < K; ++k) s = fmaf(w[k], xr[k], s);
+  rho[idx] = s;
+}
+
+}  // namespace
+
+hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, int K,
+                        int f32_inputs, hipStream_t s) {
+  if (f32_inputs) {
+    const size_t total = (size_t)B * N;
+    const size_t grid = (total + 255) / 256;
+    if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(probe_f32_kernel, dim3(grid), dim3(256), 0, s, (const float*)W,
+                       (const float*)x, rho, B, N, K);
+    return hipGetLastError();
+  }
+  const uint16_t* Wb = (const uint16_t*)W;
+  const uint16_t* xb = (const uint16_t*)x;
+  if (B > 64) {
+    dim3 grid((N + 63) / 64, (B + 63) / 64);
+    hipLaunchKernelGGL((probe_mfma_kernel<4, 4>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K);
+  } else {
+    const int mt = (B + 15) / 16;
+    dim3 grid((N + 15) / 16, 1);
+    switch (mt) {
+      case 1: hipLaunchKernelGGL((probe_mfma_kernel<1, 1>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K); break;
+      case 2: hipLaunchKernelGGL((probe_mfma_kernel<2, 1>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K); break;
+      case 3: hipLaunchKernelGGL((probe_mfma_kernel<3, 1>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K); break;
+      default: hipLaunchKernelGGL((probe_mfma_kernel<4, 1>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace parallax

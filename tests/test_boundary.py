@@ -1,0 +1,92 @@
+"""C-ABI boundary on the CPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call
+(so no GPU is needed). Also the host-side split planner."""
+import ctypes
+
+import pytest
+
+from parallax_covariance_corrected_amd import binding as pb
+
+
+@pytest.fixture(scope="module")
+def L():
+    return pb.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = pb.header_functions()
+    assert {"parallax_probe", "parallax_decode", "parallax_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _decode(L, *, q=16, rho=16, k=16, v=16, lens=16, out=16, B=2, Hq=4, Hkv=2, d=128,
+            max_ctx=64, dtype=pb.BF16):
+    # fake, never-dereferenced addresses: validation rejects before any use
+    return L.parallax_decode(q, rho, k, v, lens, out, B, Hq, Hkv, d, max_ctx, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(Hq=3, Hkv=2), pb.ERR_INVALID_ARG, "multiple"),
+    (dict(d=96), pb.ERR_UNSUPPORTED, "64 or 128"),
+    (dict(dtype=7), pb.ERR_UNSUPPORTED, "dtype"),
+    (dict(B=0), pb.ERR_INVALID_ARG, ">= 1"),
+    (dict(max_ctx=0), pb.ERR_INVALID_ARG, ">= 1"),
+    (dict(Hkv=0), pb.ERR_INVALID_ARG, ">= 1"),
+    (dict(q=0), pb.ERR_INVALID_ARG, "null"),
+    (dict(lens=0), pb.ERR_INVALID_ARG, "null"),
+    (dict(k=24), pb.ERR_INVALID_ARG, "aligned"),
+    (dict(lens=18), pb.ERR_INVALID_ARG, "aligned"),
+    (dict(max_ctx=1 << 24), pb.ERR_UNSUPPORTED, "max_ctx"),
+])
+def test_decode_rejects_bad_arguments(L, kw, code, msg):
+    assert _decode(L, **kw) == code
+    assert msg in L.parallax_last_error().decode()
+
+
+@pytest.mark.parametrize("args,code", [
+    ((16, 16, 16, 1, 2, 128, 64, 9), pb.ERR_UNSUPPORTED),     # dtype
+    ((0, 16, 16, 1, 2, 128, 64, pb.BF16), pb.ERR_INVALID_ARG),  # null W_R
+    ((16, 16, 16, 1, 2, 100, 64, pb.BF16), pb.ERR_UNSUPPORTED),  # d
+    ((16, 16, 16, 1, 2, 128, 60, pb.BF16), pb.ERR_INVALID_ARG),  # d_model % 8
+    ((16, 16, 16, 0, 2, 128, 64, pb.BF16), pb.ERR_INVALID_ARG),  # B
+    ((16, 16, 8, 1, 2, 128, 64, pb.BF16), pb.ERR_INVALID_ARG),   # misaligned rho
+])
+def test_probe_rejects_bad_arguments(L, args, code):
+    assert L.parallax_probe(*args, None) == code
+    assert L.parallax_last_error().decode()
+
+
+def test_options_and_profile_on_host(L):
+    assert L.parallax_set_option(pb.OPT_CHUNK, 100) == pb.ERR_INVALID_ARG
+    assert L.parallax_set_option(99, 0) == pb.ERR_INVALID_ARG
+    with pb.options(chunk=512, kernel=1):
+        assert pb.get_option(pb.OPT_CHUNK) == 512 and pb.get_option(pb.OPT_KERNEL) == 1
+        assert pb.decode_plan(16, 16, 8, 128, 4096) == (512, 8, 1)
+    assert pb.get_option(pb.OPT_CHUNK) == 0 and pb.get_option(pb.OPT_KERNEL) == 0
+    pb.profile_reset()
+    assert pb.profile_read(pb.KERNEL_DECODE) == (0.0, 0)
+    with pytest.raises(pb.ParallaxError):
+        pb.profile_read(5)
+
+
+def test_plan_covers_context_and_picks_kernels():
+    # (B, Hq, Hkv, d, max_ctx, dtype)
+    for shape in [(16, 16, 8, 128, 4096, pb.BF16), (1, 16, 8, 128, 32768, pb.BF16),
+                  (2048, 16, 8, 128, 128, pb.BF16), (64, 32, 8, 128, 32768, pb.BF16),
+                  (1, 2, 2, 64, 128, pb.F32), (3, 4, 4, 64, 1000, pb.BF16_F32OUT)]:
+        chunk, splits, kernel = pb.decode_plan(*shape)
+        max_ctx = shape[4]
+        assert chunk % 128 == 0 and 128 <= chunk <= 2048
+        assert (splits - 1) * chunk < max_ctx <= splits * chunk
+        assert kernel == (1 if shape[5] == pb.F32 else 2)
+    # enough workgroups for 256 compute units on the mid-context workload
+    chunk, splits, _ = pb.decode_plan(16, 16, 8, 128, 4096)
+    assert 16 * 8 * splits >= 1024
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(pb, "_lib", None)
+    monkeypatch.setattr(pb, "LIB_PATH", str(tmp_path / "libparallax.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        pb.lib()

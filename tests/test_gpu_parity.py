@@ -1,0 +1,212 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Every K/V cache is padded with NaN past each sequence length, so any read past
+seq_lens shows up as a NaN output. Tolerances: bf16 output rel-L2 <= 2e-3; the
+same kernel with an fp32 output max-abs <= 1e-2 (and bf16 output == RNE of
+that fp32 output, bitwise); fp32 path rel-L2 and max-abs <= 1e-5; probe rel-L2
+<= 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+from parallax_covariance_corrected_amd import binding as pb
+from parallax_covariance_corrected_amd.workloads import WORKLOADS, make_inputs
+
+from _gpu_common import (BF16_REL_L2, F32OUT_MAX_ABS, F32_TOL, RHO_REL_L2, Device, bf16_rne,
+                         max_abs, oracle_out, oracle_rho, rel_l2, sample_pairs, say, to64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_bf16(s, dev, rho_dev, ref, pairs=None, tag=""):
+    """bf16 and fp32-output runs of the same plan against the oracle."""
+    out16 = dev.decode(rho_dev)
+    out32 = dev.decode(rho_dev, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o16, o32 = to64(out16), to64(out32)
+    if pairs is not None:
+        o16 = np.stack([o16[b, h] for b, h in pairs])
+        o32 = np.stack([o32[b, h] for b, h in pairs])
+    assert np.isfinite(o32).all(), f"{tag}: non-finite output"
+    e16, e32, m32 = rel_l2(o16, ref), rel_l2(o32, ref), max_abs(o32, ref)
+    say(f"{tag}: rel_l2 bf16 {e16:.3e} fp32out {e32:.3e} max_abs fp32out {m32:.3e}")
+    assert e16 <= BF16_REL_L2, (tag, e16)
+    assert m32 <= F32OUT_MAX_ABS, (tag, m32)
+    np.testing.assert_array_equal(o16, bf16_rne(o32), err_msg=f"{tag}: bf16 out != RNE(fp32 out)")
+    return o32
+
+
+def _run_full_check(s, tag, pairs=None, wr_zero_too=True):
+    say(f"[case] {tag} B={s.wl.B} Hq={s.wl.Hq} Hkv={s.wl.Hkv} d={s.wl.d} "
+        f"lens[min,max]=[{int(s.seq_lens.min())},{int(s.seq_lens.max())}] seed={s.seed}")
+    dev = Device(s)
+    rho = dev.probe()
+    torch.cuda.synchronize()
+    rho_o = oracle_rho(s)
+    er = rel_l2(to64(rho), rho_o)
+    say(f"{tag}: rho rel_l2 {er:.3e}")
+    assert er <= RHO_REL_L2
+    ref = oracle_out(s, rho_o, pairs)
+    _check_bf16(s, dev, rho, ref, pairs, tag)
+    if wr_zero_too:
+        zero = torch.zeros_like(rho)
+        ref0 = oracle_out(s, np.zeros_like(rho_o), pairs)
+        _check_bf16(s, dev, zero, ref0, pairs, tag + " W_R=0")
+
+
+# ------------------------------------------------------------------ tiny fp32 workload
+def test_tiny_fp32_workload():
+    wl = WORKLOADS[1]
+    for wr_zero in (False, True):
+        s = make_inputs(wl, 0, wr_zero=wr_zero)
+        say(f"[case] tiny fp32 wr_zero={wr_zero}")
+        dev = Device(s)
+        rho = dev.probe()
+        out = dev.decode(rho)
+        torch.cuda.synchronize()
+        rho_o = oracle_rho(s)
+        ref = oracle_out(s, rho_o)
+        o = to64(out)
+        say(f"tiny fp32: rho rel {rel_l2(to64(rho), rho_o):.3e} out rel {rel_l2(o, ref):.3e} "
+            f"max_abs {max_abs(o, ref):.3e}")
+        assert rel_l2(to64(rho), rho_o) <= F32_TOL
+        assert rel_l2(o, ref) <= F32_TOL and max_abs(o, ref) <= F32_TOL
+        if wr_zero:
+            # W_R = 0 is plain softmax attention: compare with torch SDPA too
+            qt = s.q.double()[:, :, None, :]
+            kt = torch.stack([k for k in s.K]).double()
+            vt = torch.stack([v for v in s.V]).double()
+            sdpa = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, :, 0]
+            assert max_abs(o, sdpa.numpy()) <= F32_TOL
+
+
+# ------------------------------------------------------------------ bf16 workloads, reduced size
+SMALL = {
+    "gqa_mid_ctx": (WORKLOADS[2].scaled(B=3), [4096, 1000, 37]),
+    "long_ctx_full": (WORKLOADS[3], None),
+    "large_batch": (WORKLOADS[4].scaled(B=40), None),
+    "ragged_G4": (WORKLOADS[5].scaled(B=6, ctx=6000), None),
+}
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_bf16_workloads_reduced(name, seed):
+    wl, lengths = SMALL[name]
+    s = make_inputs(wl, seed, lengths=lengths)
+    _run_full_check(s, f"{name} seed{seed}")
+
+
+# ------------------------------------------------------------------ full sizes, sampled heads
+FULL = {"gqa_mid_ctx": (2, 24), "large_batch": (4, 48), "ragged_G4": (5, 24)}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_bf16_workloads_full_size_sampled(name):
+    idx, k = FULL[name]
+    s = make_inputs(WORKLOADS[idx], 0)
+    pairs = sample_pairs(s, k)
+    _run_full_check(s, f"{name} full", pairs=pairs, wr_zero_too=False)
+
+
+# ------------------------------------------------------------------ edge cases
+EDGE_LENS = [0, 1, 15, 16, 17, 127, 128, 129, 300]
+
+
+@pytest.mark.parametrize("d,Hq,Hkv,dtype", [(128, 4, 2, "bf16"), (64, 6, 2, "bf16"),
+                                            (128, 16, 2, "bf16"), (64, 3, 3, "bf16"),
+                                            (128, 4, 2, "f32"), (64, 2, 1, "f32")])
+def test_edge_lengths(d, Hq, Hkv, dtype):
+    wl = WORKLOADS[2].scaled(B=len(EDGE_LENS), Hq=Hq, Hkv=Hkv, d=d, ctx=300, d_model=256,
+                             dtype=dtype, wr_std=0.05)
+    s = make_inputs(wl, 3, lengths=EDGE_LENS)
+    tag = f"edge d={d} Hq={Hq} Hkv={Hkv} {dtype}"
+    if dtype == "bf16":
+        _run_full_check(s, tag)
+        return
+    say(f"[case] {tag}")
+    dev = Device(s)
+    rho = dev.probe()
+    out = dev.decode(rho)
+    torch.cuda.synchronize()
+    ref = oracle_out(s, oracle_rho(s))
+    o = to64(out)
+    say(f"{tag}: rel {rel_l2(o, ref):.3e} max_abs {max_abs(o, ref):.3e}")
+    assert rel_l2(o, ref) <= F32_TOL and max_abs(o, ref) <= F32_TOL
+    assert np.all(o[0] == 0.0)
+
+
+def test_zero_length_gives_zero_and_clamps_long_lengths():
+    wl = WORKLOADS[2].scaled(B=3, ctx=200, d_model=64, Hq=4, Hkv=2)
+    s = make_inputs(wl, 5, lengths=[0, 200, 200])
+    say("[case] zero length / clamp")
+    dev = Device(s)
+    dev.seq_lens = torch.tensor([0, 200, 1000], dtype=torch.int32, device="cuda")  # 1000 > max_ctx
+    rho = dev.probe()
+    out = to64(dev.decode(rho, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    assert np.all(out[0] == 0.0)
+    np.testing.assert_array_equal(out[1], out[2])   # same data, length clamped to 200
+
+
+@pytest.mark.parametrize("chunk", [128, 256, 1024, 2048])
+@pytest.mark.parametrize("kernel", [1, 2])
+def test_split_and_kernel_invariance(chunk, kernel):
+    wl = WORKLOADS[5].scaled(B=4, ctx=5000, d_model=256)
+    s = make_inputs(wl, 2, lengths=[5000, 4097, 129, 2048])
+    say(f"[case] chunk={chunk} kernel={kernel}")
+    dev = Device(s)
+    rho = dev.probe()
+    ref = oracle_out(s, oracle_rho(s))
+    with pb.options(chunk=chunk, kernel=kernel):
+        o32 = to64(dev.decode(rho, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    say(f"chunk={chunk} kernel={kernel}: rel {rel_l2(o32, ref):.3e} max_abs {max_abs(o32, ref):.3e}")
+    assert rel_l2(o32, ref) <= 1e-5 and max_abs(o32, ref) <= 1e-4
+
+
+def test_gqa_equals_replicated_mha():
+    wl = WORKLOADS[2].scaled(B=2, ctx=700, d_model=128)
+    s = make_inputs(wl, 4, lengths=[700, 333])
+    say("[case] GQA vs replicated MHA")
+    dev = Device(s)
+    rho = dev.probe()
+    gqa = to64(dev.decode(rho, out_dtype=torch.float32))
+    G = wl.Hq // wl.Hkv
+    Kr = dev.K.repeat_interleave(G, dim=1).contiguous()
+    Vr = dev.V.repeat_interleave(G, dim=1).contiguous()
+    mha = to64(pb.decode(dev.q, rho, Kr, Vr, dev.seq_lens, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    assert rel_l2(gqa, mha) <= 1e-6 and max_abs(gqa, mha) <= 1e-5
+
+
+def test_bitwise_repeatable_and_output_guards():
+    wl = WORKLOADS[2].scaled(B=4, ctx=3000, d_model=512)
+    s = make_inputs(wl, 6, lengths=[3000, 2999, 1, 640])
+    say("[case] repeatability / guards")
+    dev = Device(s)
+    rho = dev.probe()
+    n = wl.B * wl.Hq * wl.d
+    guard = 64
+    buf = torch.full((n + 2 * guard,), 12345.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[guard:guard + n].view(wl.B, wl.Hq, wl.d)
+    pb.decode(dev.q, rho, dev.K, dev.V, dev.seq_lens, out=out)
+    first = out.clone()
+    pb.decode(dev.q, rho, dev.K, dev.V, dev.seq_lens, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), out.view(torch.int16))
+    assert torch.all(buf[:guard] == 12345.0) and torch.all(buf[guard + n:] == 12345.0)
+
+
+@pytest.mark.parametrize("B,d_model,dtype", [(1, 2048, "bf16"), (17, 2560, "bf16"), (64, 2048, "bf16"),
+                                             (65, 512, "bf16"), (130, 72, "bf16"), (3, 100, "f32")])
+def test_probe_shapes(B, d_model, dtype):
+    wl = WORKLOADS[2].scaled(B=B, d_model=d_model, ctx=16, dtype=dtype)
+    s = make_inputs(wl, 7)
+    say(f"[case] probe B={B} d_model={d_model} {dtype}")
+    rho = pb.probe(s.W_R.cuda(), s.x.cuda(), wl.Hq, wl.d)
+    torch.cuda.synchronize()
+    e = rel_l2(to64(rho), oracle_rho(s))
+    say(f"probe B={B} d_model={d_model}: rel {e:.3e}")
+    assert e <= RHO_REL_L2
