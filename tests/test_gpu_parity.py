@@ -142,7 +142,10 @@ def test_zero_length_gives_zero_and_clamps_long_lengths():
     s = make_inputs(wl, 5, lengths=[0, 200, 200])
     say("[case] zero length / clamp")
     dev = Device(s)
-    dev.seq_lens = torch.tensor([0, 200, 1000], dtype=torch.int32, device="cuda")  # 1000 > max_ctx
+    # sequence 2 is a copy of sequence 1 whose length 1000 exceeds max_ctx = 200
+    for t in (dev.K, dev.V, dev.q, dev.x):
+        t[2].copy_(t[1])
+    dev.seq_lens = torch.tensor([0, 200, 1000], dtype=torch.int32, device="cuda")
     rho = dev.probe()
     out = to64(dev.decode(rho, out_dtype=torch.float32))
     torch.cuda.synchronize()
