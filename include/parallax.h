@@ -110,7 +110,9 @@ const char* parallax_last_error(void);
  * parallax_decode_plan — the launch plan parallax_decode would use (for tests
  * and measurement). Writes the chunk length in keys, the number of splits per
  * (sequence, KV head) and the decode kernel (1 = generic vector-ALU kernel,
- * 2 = matrix-core kernel). Same argument checks as parallax_decode.
+ * 2 = matrix-core kernel with four waves per work item, 3 = matrix-core
+ * kernel with one wave per work item). Same argument checks as
+ * parallax_decode.
  */
 int parallax_decode_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
                          int* chunk, int* splits, int* kernel);
@@ -118,15 +120,18 @@ int parallax_decode_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
 /*
  * Process-wide tuning options (for tests and measurement). Not to be changed
  * while other threads call the library.
- *   PARALLAX_OPT_CHUNK   : 0 = automatic, else keys per split (multiple of 128)
+ *   PARALLAX_OPT_CHUNK   : 0 = automatic, else keys per split (multiple of 64)
  *   PARALLAX_OPT_KERNEL  : 0 = automatic, 1 = force the generic kernel,
  *                          2 = force the matrix-core kernel (where supported)
  *   PARALLAX_OPT_PROFILE : 1 = record HIP events around every kernel launch
+ *   PARALLAX_OPT_ITEMS   : matrix-core work items: 0 = automatic,
+ *                          1 = four waves per item, 2 = one wave per item
  */
 typedef enum {
   PARALLAX_OPT_CHUNK = 1,
   PARALLAX_OPT_KERNEL = 2,
-  PARALLAX_OPT_PROFILE = 3
+  PARALLAX_OPT_PROFILE = 3,
+  PARALLAX_OPT_ITEMS = 4
 } parallax_option;
 
 int parallax_set_option(int option, int value);

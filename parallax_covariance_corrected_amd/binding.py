@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_MEMORY = 0, 1, 2, 3, 4
 F32, BF16, BF16_F32OUT = 0, 1, 2
-OPT_CHUNK, OPT_KERNEL, OPT_PROFILE = 1, 2, 3
+OPT_CHUNK, OPT_KERNEL, OPT_PROFILE, OPT_ITEMS = 1, 2, 3, 4
 KERNEL_PROBE, KERNEL_DECODE, KERNEL_MERGE = 0, 1, 2
 
 _lib = None
@@ -167,7 +167,8 @@ class options:
     """Context manager that sets library options and restores them on exit."""
 
     def __init__(self, **kw):
-        self.kw = {{"chunk": OPT_CHUNK, "kernel": OPT_KERNEL, "profile": OPT_PROFILE}[k]: v
+        self.kw = {{"chunk": OPT_CHUNK, "kernel": OPT_KERNEL, "profile": OPT_PROFILE,
+                    "items": OPT_ITEMS}[k]: v
                    for k, v in kw.items()}
         self.saved = {}
 

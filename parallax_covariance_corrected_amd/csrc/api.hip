@@ -29,6 +29,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int g_opt_chunk = 0;
 int g_opt_kernel = 0;
 int g_opt_profile = 0;
+int g_opt_items = 0;
 
 // ---------------------------------------------------------------- profiling
 struct Timing {
@@ -80,7 +81,7 @@ struct KernelTimer {
 struct Plan {
   int chunk;
   int splits;
-  int kernel;   // 1 generic, 2 matrix-core
+  int kernel;   // 1 generic, 2 matrix-core workgroup items, 3 matrix-core wave items
 };
 
 int esize(int dtype) { return dtype == PARALLAX_F32 ? 4 : 2; }
@@ -105,17 +106,28 @@ int check_decode_shape(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
 Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
   Plan p;
   const int G = Hq / Hkv;
-  p.kernel = (dtype == PARALLAX_F32) ? 1 : 2;
-  if (g_opt_kernel == 1) p.kernel = 1;
-  if (g_opt_kernel == 2 && dtype != PARALLAX_F32 && parallax::decode_mfma_supported(d, G)) p.kernel = 2;
+  const bool mfma_ok = dtype != PARALLAX_F32 && parallax::decode_mfma_supported(d, G);
+  bool mfma = mfma_ok;
+  if (g_opt_kernel == 1) mfma = false;
+  const int GH = G <= 4 ? G : (G % 4 == 0 ? 4 : (G % 3 == 0 ? 3 : (G % 2 == 0 ? 2 : 1)));
+  const long long units = (long long)B * Hkv * (mfma ? G / GH : 1);
+  // Wave items (one wave per item) suit many short sequences; workgroup items
+  // (four waves per item) suit long ones.
+  bool wave_items = mfma && units >= 1024 && max_ctx <= 1024;
+  if (mfma && g_opt_items == 1) wave_items = false;
+  if (mfma && g_opt_items == 2) wave_items = true;
+  p.kernel = !mfma ? 1 : (wave_items ? 3 : 2);
   int chunk = g_opt_chunk;
   if (chunk <= 0) {
-    // Enough workgroups to keep every CU busy (~2048), chunks of 128..2048 keys.
-    const long long units = (long long)B * Hkv;
-    const long long want = units >= 2048 ? 1 : (2048 + units - 1) / units;
+    // Enough items to fill 256 compute units (2048 waves or 512 workgroups),
+    // chunks of 64 (wave items) / 128 (workgroup items) to 2048 keys so that a
+    // ragged batch stays balanced.
+    const long long target = wave_items ? 2048 : 512;
+    const long long want = units >= target ? 1 : (target + units - 1) / units;
     long long c = (max_ctx + want - 1) / want;
-    c = (c + 127) / 128 * 128;
-    if (c < 128) c = 128;
+    c = (c + 63) / 64 * 64;
+    const long long lo = wave_items ? 64 : 128;
+    if (c < lo) c = lo;
     if (c > 2048) c = 2048;
     chunk = (int)c;
   }
@@ -133,8 +145,8 @@ const char* parallax_last_error(void) { return g_last_error.c_str(); }
 int parallax_set_option(int option, int value) {
   switch (option) {
     case PARALLAX_OPT_CHUNK:
-      if (value < 0 || value % 128 != 0)
-        return fail(PARALLAX_ERR_INVALID_ARG, "chunk must be 0 or a positive multiple of 128");
+      if (value < 0 || value % 64 != 0)
+        return fail(PARALLAX_ERR_INVALID_ARG, "chunk must be 0 or a positive multiple of 64");
       g_opt_chunk = value;
       return PARALLAX_OK;
     case PARALLAX_OPT_KERNEL:
@@ -144,6 +156,10 @@ int parallax_set_option(int option, int value) {
     case PARALLAX_OPT_PROFILE:
       if (value != 0 && value != 1) return fail(PARALLAX_ERR_INVALID_ARG, "profile must be 0 or 1");
       g_opt_profile = value;
+      return PARALLAX_OK;
+    case PARALLAX_OPT_ITEMS:
+      if (value < 0 || value > 2) return fail(PARALLAX_ERR_INVALID_ARG, "items must be 0, 1 or 2");
+      g_opt_items = value;
       return PARALLAX_OK;
     default:
       return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
@@ -156,6 +172,7 @@ int parallax_get_option(int option, int* value) {
     case PARALLAX_OPT_CHUNK: *value = g_opt_chunk; return PARALLAX_OK;
     case PARALLAX_OPT_KERNEL: *value = g_opt_kernel; return PARALLAX_OK;
     case PARALLAX_OPT_PROFILE: *value = g_opt_profile; return PARALLAX_OK;
+    case PARALLAX_OPT_ITEMS: *value = g_opt_items; return PARALLAX_OK;
     default: return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
   }
 }
@@ -275,7 +292,7 @@ int parallax_decode(const void* q, const float* rho, const void* k_cache, const 
   hipError_t e;
   {
     KernelTimer tm(1, stream);
-    e = (p.kernel == 2) ? parallax::launch_decode_mfma(a, d, stream)
+    e = (p.kernel >= 2) ? parallax::launch_decode_mfma(a, d, p.kernel == 3 ? 1 : 0, stream)
                         : parallax::launch_decode_generic(a, d, dtype == PARALLAX_F32 ? 1 : 0, stream);
     tm.finish();
   }

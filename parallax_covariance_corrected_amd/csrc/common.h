@@ -23,13 +23,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(((unsigned)b) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+// fp32 -> bf16 bits, round to nearest even (the hardware conversion).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  unsigned u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  unsigned lsb = (u >> 16) & 1u;
-  u += 0x7fffu + lsb;
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return (unsigned)f32_to_bf16_rne(lo) | ((unsigned)f32_to_bf16_rne(hi) << 16);
 }
 
 // Raw buffer resource over [base, base + bytes): loads at byte offsets past
@@ -92,7 +92,7 @@ struct DecodeArgs {
 
 // Internal launchers (one translation unit each). Return hipError_t.
 hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, hipStream_t s);
 bool decode_mfma_supported(int d, int G);
 hipError_t launch_merge(const DecodeArgs& a, int d, hipStream_t s);
 hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, int K,

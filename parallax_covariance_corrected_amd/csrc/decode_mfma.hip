@@ -8,32 +8,38 @@
 // with both branches fed by one read of each K/V row (same paragraph: the KV
 // stream is shared, which is what doubles the arithmetic intensity).
 //
-// Work decomposition: one workgroup (4 waves) per (sequence, KV head, head
-// block, split of `chunk` keys). A wave takes 32 keys per step (two 16-key
-// tiles), steps strided by 128 keys, with the next step's K/V prefetched into
-// registers. K/V rows are read with raw buffer loads whose range ends at the
-// last key of the split, so the ragged tail reads zeros without touching
-// memory (and never reads past seq_lens).
+// Work items. An item is (sequence, KV head, head block of GH query heads,
+// split of `chunk` keys). Two decompositions share the same tile code:
+//  * workgroup items (long contexts): the 4 waves of a workgroup take
+//    interleaved 16-key tiles of one item and merge their states in LDS;
+//  * wave items (short contexts, many sequences): every wave owns one item,
+//    so a workgroup serves 4 items with no cross-wave merge.
+// An item with one split writes the output; otherwise it writes its partial
+// state (m, l, S, A, P) for the merge kernel.
 //
-// Per 16-key tile:
-//  * scores and probes: one bf16 16x16x32 MFMA product  K_tile (16 keys x 32
-//    dims) . X^T (32 dims x 16 columns)  per 32 dims, where the columns of X are
-//    q of each head (exact: bf16 x bf16 products are exact in fp32) and rho of
-//    each head split as rho_hi + rho_lo (two bf16 operands accumulated into the
-//    same fp32 result), so rho keeps ~16 significant bits.
-//    Lane l receives 4 keys (4*(l/16) + r) of one column (l % 16).
+// Per wave, 16-key tiles stream through a 3-deep register ring: the loads of
+// tiles t+1 and t+2 are in flight while tile t is computed. K/V rows are read
+// with raw buffer loads whose range ends at the last key of the item, so the
+// ragged tail reads zeros without touching memory and nothing past seq_lens is
+// ever read.
+//
+// Per tile:
+//  * scores and probes: one bf16 16x16x32 MFMA product K_tile (16 keys x 32
+//    dims) . X^T (32 dims x 16 columns) per 32 dims; the columns of X are q of
+//    each head (exact: bf16 x bf16 products are exact in fp32) and rho of each
+//    head split as rho_hi + rho_lo (two bf16 operands accumulated into the same
+//    fp32 result, so rho keeps ~16 significant bits). Lane l receives keys
+//    4*(l/16) + r, r = 0..3, of column l % 16.
 //  * online softmax with a lazy rescale: the running max moves only when a
-//    tile max exceeds it by more than 8 (log2 units), so e <= 2^8 between
-//    rescales and almost every tile skips the rescale.
-//  * weights: e for the score columns, e*p for the probe columns, moved next to
-//    each other with DPP lane moves inside 4- or 16-lane rows.
+//    score exceeds it by more than 8 (log2 units), so e <= 2^8 between
+//    rescales; the common path needs no cross-lane reduction.
+//  * weights: e for the score columns, e*p for the probe columns, moved next
+//    to each other with DPP lane moves inside 4- or 16-lane rows.
 //  * weighted value sums: fp32 4x4x1 MFMA blocks (16 blocks per instruction):
-//    A operand = the weight rows (e_h, e_h p_h) of one key, B operand = 4
-//    value dims of that key, so weights stay fp32 (a bf16 weight would cost
+//    A operand = the weight rows (e_h, e_h p_h) of one key, B operand = one
+//    value dim of that key, so weights stay fp32 (a bf16 weight would cost
 //    about 1e-3 relative error) and V needs no transpose: each lane's 16-byte
 //    V load supplies 8 consecutive dims.
-// Wave states are merged in LDS; with one split the workgroup writes out,
-// otherwise it writes its partial (m, l, S, A, P) for the merge kernel.
 #include <type_traits>
 
 #include "common.h"
@@ -75,9 +81,9 @@ struct KV {
   static constexpr int EPV = D / 16;   // value dims per lane
   static constexpr int ROW = 2 * D;    // bytes per cache row
   using VW = typename std::conditional<D == 128, u32x4, u32x2>::type;
-  struct Step {
-    u32x4 k[2][NC];
-    VW v[2][4];
+  struct Tile {
+    u32x4 k[NC];
+    VW v[4];
   };
   __device__ static VW vload(__amdgpu_buffer_rsrc_t r, unsigned off) {
     if constexpr (D == 128) return buf_load16(r, off);
@@ -88,27 +94,50 @@ struct KV {
   }
 };
 
-template <int D, int GH>
+template <int D, int GH, bool WAVE_ITEM>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   using L = Layout<GH>;
   using C = KV<D>;
   constexpr int NC = C::NC, EPV = C::EPV, ROW = C::ROW, NSET = L::NSET;
+  constexpr int STRIDE = WAVE_ITEM ? 16 : 64;   // keys between a wave's tiles
 
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = a.Hq / a.Hkv;
   const int hblocks = G / GH;
-  int wg = blockIdx.x;
-  const int split = wg % a.splits; wg /= a.splits;
-  const int hb = wg % hblocks; wg /= hblocks;
-  const int kvh = wg % a.Hkv;
-  const int b = wg / a.Hkv;
+  int item = WAVE_ITEM ? blockIdx.x * 4 + wave : blockIdx.x;
+  if (WAVE_ITEM && item >= a.B * a.Hkv * hblocks * a.splits) return;
+  const int split = item % a.splits; item /= a.splits;
+  const int hb = item % hblocks; item /= hblocks;
+  const int kvh = item % a.Hkv;
+  const int b = item / a.Hkv;
   const int n = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int c0 = split * a.chunk;
   if (a.splits > 1 && c0 >= n) return;   // empty split: the merge never reads it
   const int c1 = min(c0 + a.chunk, n);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4, quad = l16 >> 2, qi = lane & 3;
   const int h0 = kvh * G + hb * GH;
+
+  // K/V streams of this (sequence, KV head), ranged to [0, c1).
+  const size_t seq = ((size_t)b * a.Hkv + kvh) * (size_t)a.max_ctx;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc((const char*)a.k + seq * ROW, (unsigned)c1 * ROW);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const char*)a.v + seq * ROW, (unsigned)c1 * ROW);
+  const unsigned koff = l16 * ROW + 16 * grp;
+  const unsigned voff = 4 * grp * ROW + l16 * (ROW / 16);
+  auto load = [&](typename C::Tile& t, int j) {
+    const unsigned base = (unsigned)j * ROW;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) t.k[c] = buf_load16(krs, base + koff + 64 * c);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t.v[c] = C::vload(vrs, base + voff + c * ROW);
+  };
+
+  // Start streaming before the q/rho prologue so the latencies overlap.
+  typename C::Tile t0, t1, t2;
+  int j = c0 + (WAVE_ITEM ? 0 : 16 * wave);
+  load(t0, j);
+  load(t1, j + STRIDE);
 
   // Column role of this lane in the score/probe product.
   bool is_s, is_p;
@@ -123,8 +152,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     chead = qi;
   }
 
-  // B operands: column vector (q, or rho split hi + lo) at dims 32c + 8*grp + t.
-  bf16x8 bhi[NC], blo[NC];
+  // B operands: column vector (q, or rho split hi + lo) at dims 32c + 8*grp + t,
+  // staged in this wave's LDS slot and re-read per tile (keeps VGPRs free for
+  // loads in flight).
+  __shared__ u32x4 sB[4][2][NC][64];
   {
     const size_t bh = (size_t)b * a.Hq + h0 + chead;
 #pragma unroll
@@ -139,35 +170,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         const float r[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint16_t h_a = f32_to_bf16_rne(r[2 * w]), h_b = f32_to_bf16_rne(r[2 * w + 1]);
-          const uint16_t l_a = f32_to_bf16_rne(r[2 * w] - bf16_bits_to_f32(h_a));
-          const uint16_t l_b = f32_to_bf16_rne(r[2 * w + 1] - bf16_bits_to_f32(h_b));
-          hi[w] = (unsigned)h_a | ((unsigned)h_b << 16);
-          lo[w] = (unsigned)l_a | ((unsigned)l_b << 16);
+          hi[w] = pack_bf16x2(r[2 * w], r[2 * w + 1]);
+          lo[w] = pack_bf16x2(r[2 * w] - bf16_lo(hi[w]), r[2 * w + 1] - bf16_hi(hi[w]));
         }
       }
-      bhi[c] = as_bf16x8(hi);
-      blo[c] = as_bf16x8(lo);
+      sB[wave][0][c][lane] = hi;
+      sB[wave][1][c][lane] = lo;
     }
   }
-
-  const size_t seq = ((size_t)b * a.Hkv + kvh) * (size_t)a.max_ctx;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc((const char*)a.k + seq * ROW, (unsigned)c1 * ROW);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const char*)a.v + seq * ROW, (unsigned)c1 * ROW);
-  const unsigned koff = l16 * ROW + 16 * grp;
-  const unsigned voff = 4 * grp * ROW + l16 * (ROW / 16);
-
-  auto load = [&](typename C::Step& st, int j) {
-    const unsigned base = (unsigned)j * ROW;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) st.k[u][c] = buf_load16(krs, base + u * 16 * ROW + koff + 64 * c);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) st.v[u][c] = C::vload(vrs, base + u * 16 * ROW + voff + c * ROW);
-  };
 
   float m_run = kNegInf;      // running max (log2 domain), score lanes
   float lsum = 0.f, ssum = 0.f;
@@ -177,33 +187,34 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < EPV; ++t) acc[s][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const typename C::Step& st, int j) {
-    float val[2][4];
+  auto compute = [&](const typename C::Tile& tl, int jt) {
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[u][c]), bhi[c], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.k[u][c]), blo[c], sacc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) val[u][r] = sacc[r];
+    for (int c = 0; c < NC; ++c) {
+      const bf16x8 bhi = as_bf16x8(sB[wave][0][c][lane]);
+      const bf16x8 blo = as_bf16x8(sB[wave][1][c][lane]);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[c]), bhi, sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[c]), blo, sacc, 0, 0, 0);
     }
-    float x[2][4];
-    float tmax = kNegInf;
+    float x[4];
+    float lmax = kNegInf;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int r = 0; r < 4; ++r) {
+      x[r] = is_s ? sacc[r] * a.scale_log2 : kNegInf;
+      lmax = fmaxf(lmax, x[r]);
+    }
+    if (jt + 16 > c1) {   // last tile of the item: mask keys past its end
+      lmax = kNegInf;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = j + 16 * u + 4 * grp + r;
-        x[u][r] = (is_s && key < c1) ? val[u][r] * a.scale_log2 : kNegInf;
-        tmax = fmaxf(tmax, x[u][r]);
+        if (jt + 4 * grp + r >= c1) x[r] = kNegInf;
+        lmax = fmaxf(lmax, x[r]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const bool need = is_s && (tmax > m_run + kRescaleThreshold);
-    if (__any(need)) {
+    }
+    if (__any(is_s && lmax > m_run + kRescaleThreshold)) {
+      float tmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const bool need = is_s && tmax > m_run + kRescaleThreshold;
       const float mnew = need ? tmax : m_run;
       const float alpha = need ? rescale(m_run, mnew) : 1.f;
       if (is_s) m_run = mnew;
@@ -228,54 +239,50 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       lsum *= a0;
       ssum *= a1;
     }
-    float w0[2][4], w1[2][4];
+    float w0[4], w1[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = is_s ? fast_exp2(x[u][r] - m_run) : 0.f;
-        if constexpr (GH <= 2) {
-          constexpr int kQuadPerm = GH == 2 ? 0x44 : 0x00;   // lane qi reads lane qi - GH
-          const float esrc = dpp<kQuadPerm>(e);
-          w0[u][r] = is_s ? e : (is_p ? esrc * val[u][r] : 0.f);
-          lsum += w0[u][r];
-        } else {
-          const float efrom = dpp<kDppRowShr8>(e);
-          const float ep = efrom * val[u][r];
-          const float epto = dpp<kDppRowShl8>(ep);
-          w0[u][r] = is_s ? e : (is_p ? efrom : 0.f);
-          w1[u][r] = is_s ? epto : (is_p ? ep : 0.f);
-          lsum += w0[u][r];
-          ssum += w1[u][r];
-        }
+    for (int r = 0; r < 4; ++r) {
+      const float e = is_s ? fast_exp2(x[r] - m_run) : 0.f;
+      if constexpr (GH <= 2) {
+        constexpr int kQuadPerm = GH == 2 ? 0x44 : 0x00;   // lane qi reads lane qi - GH
+        const float esrc = dpp<kQuadPerm>(e);
+        w0[r] = is_s ? e : (is_p ? esrc * sacc[r] : 0.f);
+        lsum += w0[r];
+      } else {
+        const float efrom = dpp<kDppRowShr8>(e);
+        const float ep = efrom * sacc[r];
+        const float epto = dpp<kDppRowShl8>(ep);
+        w0[r] = is_s ? e : (is_p ? efrom : 0.f);
+        w1[r] = is_s ? epto : (is_p ? ep : 0.f);
+        lsum += w0[r];
+        ssum += w1[r];
       }
+    }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int t = 0; t < EPV; ++t) {
-          const float vf = C::velem(st.v[u][c], t);
-          acc[0][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w0[u][c], vf, acc[0][t], 0, 0, 0);
-          if constexpr (NSET > 1)
-            acc[1][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w1[u][c], vf, acc[1][t], 0, 0, 0);
-        }
+      for (int t = 0; t < EPV; ++t) {
+        const float vf = C::velem(tl.v[c], t);
+        acc[0][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w0[c], vf, acc[0][t], 0, 0, 0);
+        if constexpr (NSET > 1)
+          acc[1][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w1[c], vf, acc[1][t], 0, 0, 0);
       }
+    }
   };
 
-  {
-    typename C::Step sa, sb;
-    int j = c0 + 32 * wave;
-    load(sa, j);
-    while (j < c1) {
-      load(sb, j + 128);
-      compute(sa, j);
-      j += 128;
-      if (j >= c1) break;
-      load(sa, j + 128);
-      compute(sb, j);
-      j += 128;
-    }
+  // Three-deep ring: compute tile t while tiles t+1, t+2 are loading.
+  while (j < c1) {
+    load(t2, j + 2 * STRIDE);
+    compute(t0, j);
+    j += STRIDE;
+    if (j >= c1) break;
+    load(t0, j + 2 * STRIDE);
+    compute(t1, j);
+    j += STRIDE;
+    if (j >= c1) break;
+    load(t1, j + 2 * STRIDE);
+    compute(t2, j);
+    j += STRIDE;
   }
 
   // Sum the four key slots (lane groups of 16) of this wave.
@@ -297,51 +304,93 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         acc[s][t][r] = v;
       }
 
-  __shared__ float sA[4][GH][D], sP[4][GH][D], sM[4][GH], sL[4][GH], sS[4][GH];
-  if (grp == 0) {
+  if constexpr (WAVE_ITEM) {
+    // This wave holds the whole item: per-head m, l, S from the score lanes.
+    float mh[GH], lh[GH], sh[GH];
 #pragma unroll
-    for (int s = 0; s < NSET; ++s)
+    for (int h = 0; h < GH; ++h) {
+      mh[h] = readlane_f(m_run, h);
+      lh[h] = readlane_f(lsum, h);
+      sh[h] = (GH <= 2) ? readlane_f(lsum, GH + h) : readlane_f(ssum, h);
+    }
+    if (grp == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = L::head(s, r);
-        if (h < 0) continue;
+      for (int h = 0; h < GH; ++h) {
+        const size_t bh = (size_t)b * a.Hq + h0 + h;
 #pragma unroll
         for (int t = 0; t < EPV; ++t) {
-          if (L::is_A(s, r)) sA[wave][h][l16 * EPV + t] = acc[s][t][r];
-          else sP[wave][h][l16 * EPV + t] = acc[s][t][r];
+          float Av = 0.f, Pv = 0.f;
+#pragma unroll
+          for (int s = 0; s < NSET; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (L::head(s, r) != h) continue;
+              if (L::is_A(s, r)) Av = acc[s][t][r];
+              else Pv = acc[s][t][r];
+            }
+          const int i = l16 * EPV + t;
+          if (a.splits == 1) {
+            const float o = parallax_out(Av, Pv, lh[h], sh[h]);
+            if (a.out_f32) store_out<float>((float*)a.out + bh * D + i, o);
+            else store_out<uint16_t>((uint16_t*)a.out + bh * D + i, o);
+          } else {
+            const size_t ps = bh * a.splits + split;
+            a.ap[ps * 2 * D + i] = Av;
+            a.ap[ps * 2 * D + D + i] = Pv;
+          }
         }
+        if (a.splits > 1 && l16 == 0)
+          a.ml[bh * a.splits + split] = make_float4(mh[h], lh[h], sh[h], 0.f);
       }
-    if (lane < GH) sM[wave][lane] = m_run;
-    if constexpr (GH <= 2) {
-      if (lane < GH) sL[wave][lane] = lsum;
-      else if (lane < 2 * GH) sS[wave][lane - GH] = lsum;
-    } else {
-      if (lane < GH) { sL[wave][lane] = lsum; sS[wave][lane] = ssum; }
     }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < GH * D; idx += 256) {
-    const int h = idx / D, i = idx % D;
-    float M = sM[0][h];
+    return;
+  } else {
+    __shared__ float sA[4][GH][D], sP[4][GH][D], sM[4][GH], sL[4][GH], sS[4][GH];
+    if (grp == 0) {
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sM[w][h]);
-    float lt = 0.f, St = 0.f, At = 0.f, Pt = 0.f;
+      for (int s = 0; s < NSET; ++s)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float c = rescale(sM[w][h], M);
-      lt = fmaf(c, sL[w][h], lt); St = fmaf(c, sS[w][h], St);
-      At = fmaf(c, sA[w][h][i], At); Pt = fmaf(c, sP[w][h][i], Pt);
+        for (int r = 0; r < 4; ++r) {
+          const int h = L::head(s, r);
+          if (h < 0) continue;
+#pragma unroll
+          for (int t = 0; t < EPV; ++t) {
+            if (L::is_A(s, r)) sA[wave][h][l16 * EPV + t] = acc[s][t][r];
+            else sP[wave][h][l16 * EPV + t] = acc[s][t][r];
+          }
+        }
+      if (lane < GH) sM[wave][lane] = m_run;
+      if constexpr (GH <= 2) {
+        if (lane < GH) sL[wave][lane] = lsum;
+        else if (lane < 2 * GH) sS[wave][lane - GH] = lsum;
+      } else {
+        if (lane < GH) { sL[wave][lane] = lsum; sS[wave][lane] = ssum; }
+      }
     }
-    const size_t bh = (size_t)b * a.Hq + h0 + h;
-    if (a.splits == 1) {
-      const float o = parallax_out(At, Pt, lt, St);
-      if (a.out_f32) store_out<float>((float*)a.out + bh * D + i, o);
-      else store_out<uint16_t>((uint16_t*)a.out + bh * D + i, o);
-    } else {
-      const size_t ps = bh * a.splits + split;
-      a.ap[ps * 2 * D + i] = At;
-      a.ap[ps * 2 * D + D + i] = Pt;
-      if (i == 0) a.ml[ps] = make_float4(M, lt, St, 0.f);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < GH * D; idx += 256) {
+      const int h = idx / D, i = idx % D;
+      float M = sM[0][h];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, sM[w][h]);
+      float lt = 0.f, St = 0.f, At = 0.f, Pt = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float c = rescale(sM[w][h], M);
+        lt = fmaf(c, sL[w][h], lt); St = fmaf(c, sS[w][h], St);
+        At = fmaf(c, sA[w][h][i], At); Pt = fmaf(c, sP[w][h][i], Pt);
+      }
+      const size_t bh = (size_t)b * a.Hq + h0 + h;
+      if (a.splits == 1) {
+        const float o = parallax_out(At, Pt, lt, St);
+        if (a.out_f32) store_out<float>((float*)a.out + bh * D + i, o);
+        else store_out<uint16_t>((uint16_t*)a.out + bh * D + i, o);
+      } else {
+        const size_t ps = bh * a.splits + split;
+        a.ap[ps * 2 * D + i] = At;
+        a.ap[ps * 2 * D + D + i] = Pt;
+        if (i == 0) a.ml[ps] = make_float4(M, lt, St, 0.f);
+      }
     }
   }
 }
@@ -354,17 +403,18 @@ int head_block(int G) {
   return 1;
 }
 
-template <int D>
-hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+template <int D, bool WI>
+hipError_t launch_dw(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int GH = head_block(G);
-  const size_t grid = (size_t)a.B * a.Hkv * (G / GH) * a.splits;
-  if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const size_t items = (size_t)a.B * a.Hkv * (G / GH) * a.splits;
+  const size_t grid = WI ? (items + 3) / 4 : items;
+  if (grid > 0x7fffffffu || items > 0x7fffffffu) return hipErrorInvalidConfiguration;
   switch (GH) {
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4>), dim3(grid), dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<D, 3>), dim3(grid), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<D, 2>), dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_mfma_kernel<D, 1>), dim3(grid), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4, WI>), dim3(grid), dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<D, 3, WI>), dim3(grid), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<D, 2, WI>), dim3(grid), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_mfma_kernel<D, 1, WI>), dim3(grid), dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -373,8 +423,9 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 
 bool decode_mfma_supported(int d, int G) { return (d == 64 || d == 128) && G >= 1; }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
-  return d == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, hipStream_t s) {
+  if (wave_items) return d == 64 ? launch_dw<64, true>(a, s) : launch_dw<128, true>(a, s);
+  return d == 64 ? launch_dw<64, false>(a, s) : launch_dw<128, false>(a, s);
 }
 
 }  // namespace parallax

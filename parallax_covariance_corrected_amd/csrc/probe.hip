@@ -8,9 +8,10 @@
 // or LDS staging of operands is needed. Products of bf16 values are exact in
 // fp32 and the accumulation is fp32.
 //
-// bf16 kernel: a workgroup (4 waves) owns a (16*MT rows) x (16*NT columns)
-// tile; its waves split K four ways (32-wide steps strided by 128) and reduce
-// through LDS in a fixed order. Rows past B read zeros (buffer range).
+// bf16 kernel: a workgroup of NW waves owns a (16*MT rows) x (16*NT columns)
+// tile; its waves split K NW ways, each issuing the loads of U k-steps before
+// their MFMAs, and reduce through LDS in a fixed order. Rows past B read zeros
+// (buffer range).
 // fp32 kernel: one thread per output, a plain dot product.
 #include "common.h"
 
@@ -19,11 +20,11 @@ namespace {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-template <int MT, int NT>
-__global__ __launch_bounds__(256) void probe_mfma_kernel(const uint16_t* __restrict__ W,
-                                                         const uint16_t* __restrict__ x,
-                                                         float* __restrict__ rho, int B, int N,
-                                                         int K) {
+template <int MT, int NT, int NW, int U>
+__global__ __launch_bounds__(NW * 64) void probe_mfma_kernel(const uint16_t* __restrict__ W,
+                                                             const uint16_t* __restrict__ x,
+                                                             float* __restrict__ rho, int B, int N,
+                                                             int K) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int n0 = blockIdx.x * 16 * NT;
@@ -40,25 +41,32 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(const uint16_t* __restr
 #pragma unroll
     for (int jn = 0; jn < NT; ++jn) acc[i][jn] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-
-  for (int k0 = 32 * wave; k0 < K; k0 += 128) {
-    u32x4 xa[MT], wb[NT];
-    // K % 8 == 0, so an 8-wide group is entirely inside or past the row; a
-    // group past the row gets an offset beyond the buffer range and reads 0.
-    const unsigned koff = (k0 + 8 * grp < K) ? (unsigned)(k0 + 8 * grp) * 2 : 0x80000000u;
+  // The NW waves split K into 32-wide steps (wave w takes steps w, w + NW, ...);
+  // each wave issues the loads of U steps before their MFMAs.
+  for (int k0 = 32 * wave; k0 < K; k0 += 32 * NW * U) {
+    u32x4 xa[U][MT], wb[U][NT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) xa[i] = buf_load16(xr, (unsigned)(16 * i + l16) * rowb + koff);
+    for (int u = 0; u < U; ++u) {
+      const int kk = k0 + u * 32 * NW + 8 * grp;
+      // K % 8 == 0: an 8-wide group is entirely inside or past the row; a group
+      // past the row gets an offset beyond the buffer range and reads 0.
+      const unsigned koff = kk < K ? (unsigned)kk * 2 : 0x80000000u;
 #pragma unroll
-    for (int jn = 0; jn < NT; ++jn) wb[jn] = buf_load16(wr, (unsigned)(16 * jn + l16) * rowb + koff);
+      for (int i = 0; i < MT; ++i) xa[u][i] = buf_load16(xr, (unsigned)(16 * i + l16) * rowb + koff);
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int jn = 0; jn < NT; ++jn) wb[u][jn] = buf_load16(wr, (unsigned)(16 * jn + l16) * rowb + koff);
+    }
 #pragma unroll
-      for (int jn = 0; jn < NT; ++jn)
-        acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[i]), as_bf16x8(wb[jn]),
-                                                              acc[i][jn], 0, 0, 0);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int jn = 0; jn < NT; ++jn)
+          acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[u][i]), as_bf16x8(wb[u][jn]),
+                                                                acc[i][jn], 0, 0, 0);
   }
 
-  __shared__ f32x4 red[3][MT * NT][64];
+  __shared__ f32x4 red[NW - 1][MT * NT][64];
   if (wave > 0) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(const uint16_t* __restr
       for (int jn = 0; jn < NT; ++jn) {
         f32x4 v = acc[i][jn];
 #pragma unroll
-        for (int w = 0; w < 3; ++w) {
+        for (int w = 0; w < NW - 1; ++w) {
           const f32x4 o = red[w][i * NT + jn][lane];
           v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
         }
@@ -117,15 +125,15 @@ hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, 
   const uint16_t* xb = (const uint16_t*)x;
   if (B > 64) {
     dim3 grid((N + 63) / 64, (B + 63) / 64);
-    hipLaunchKernelGGL((probe_mfma_kernel<4, 4>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K);
+    hipLaunchKernelGGL((probe_mfma_kernel<4, 4, 4, 2>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K);
   } else {
     const int mt = (B + 15) / 16;
     dim3 grid((N + 15) / 16, 1);
     switch (mt) {
-      case 1: hipLaunchKernelGGL((probe_mfma_kernel<1, 1>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K); break;
-      case 2: hipLaunchKernelGGL((probe_mfma_kernel<2, 1>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K); break;
-      case 3: hipLaunchKernelGGL((probe_mfma_kernel<3, 1>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K); break;
-      default: hipLaunchKernelGGL((probe_mfma_kernel<4, 1>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K); break;
+      case 1: hipLaunchKernelGGL((probe_mfma_kernel<1, 1, 8, 8>), grid, dim3(512), 0, s, Wb, xb, rho, B, N, K); break;
+      case 2: hipLaunchKernelGGL((probe_mfma_kernel<2, 1, 8, 4>), grid, dim3(512), 0, s, Wb, xb, rho, B, N, K); break;
+      case 3: hipLaunchKernelGGL((probe_mfma_kernel<3, 1, 8, 4>), grid, dim3(512), 0, s, Wb, xb, rho, B, N, K); break;
+      default: hipLaunchKernelGGL((probe_mfma_kernel<4, 1, 8, 4>), grid, dim3(512), 0, s, Wb, xb, rho, B, N, K); break;
     }
   }
   return hipGetLastError();

@@ -59,10 +59,13 @@ def test_probe_rejects_bad_arguments(L, args, code):
 
 def test_options_and_profile_on_host(L):
     assert L.parallax_set_option(pb.OPT_CHUNK, 100) == pb.ERR_INVALID_ARG
+    assert L.parallax_set_option(pb.OPT_ITEMS, 3) == pb.ERR_INVALID_ARG
     assert L.parallax_set_option(99, 0) == pb.ERR_INVALID_ARG
     with pb.options(chunk=512, kernel=1):
         assert pb.get_option(pb.OPT_CHUNK) == 512 and pb.get_option(pb.OPT_KERNEL) == 1
         assert pb.decode_plan(16, 16, 8, 128, 4096) == (512, 8, 1)
+    with pb.options(items=2, chunk=256):
+        assert pb.decode_plan(16, 16, 8, 128, 4096) == (256, 16, 3)
     assert pb.get_option(pb.OPT_CHUNK) == 0 and pb.get_option(pb.OPT_KERNEL) == 0
     pb.profile_reset()
     assert pb.profile_read(pb.KERNEL_DECODE) == (0.0, 0)
@@ -77,12 +80,15 @@ def test_plan_covers_context_and_picks_kernels():
                   (1, 2, 2, 64, 128, pb.F32), (3, 4, 4, 64, 1000, pb.BF16_F32OUT)]:
         chunk, splits, kernel = pb.decode_plan(*shape)
         max_ctx = shape[4]
-        assert chunk % 128 == 0 and 128 <= chunk <= 2048
+        assert chunk % 64 == 0 and 64 <= chunk <= 2048
         assert (splits - 1) * chunk < max_ctx <= splits * chunk
-        assert kernel == (1 if shape[5] == pb.F32 else 2)
+        assert kernel == 1 if shape[5] == pb.F32 else kernel in (2, 3)
+    # many short sequences: one wave per item; long ones: four waves per item
+    assert pb.decode_plan(2048, 16, 8, 128, 128)[2] == 3
+    assert pb.decode_plan(16, 16, 8, 128, 4096)[2] == 2
     # enough workgroups for 256 compute units on the mid-context workload
     chunk, splits, _ = pb.decode_plan(16, 16, 8, 128, 4096)
-    assert 16 * 8 * splits >= 1024
+    assert 16 * 8 * splits >= 512
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

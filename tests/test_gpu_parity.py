@@ -153,16 +153,16 @@ def test_zero_length_gives_zero_and_clamps_long_lengths():
     np.testing.assert_array_equal(out[1], out[2])   # same data, length clamped to 200
 
 
-@pytest.mark.parametrize("chunk", [128, 256, 1024, 2048])
-@pytest.mark.parametrize("kernel", [1, 2])
-def test_split_and_kernel_invariance(chunk, kernel):
+@pytest.mark.parametrize("chunk", [64, 128, 256, 1024, 2048])
+@pytest.mark.parametrize("kernel,items", [(1, 0), (2, 1), (2, 2)])
+def test_split_and_kernel_invariance(chunk, kernel, items):
     wl = WORKLOADS[5].scaled(B=4, ctx=5000, d_model=256)
     s = make_inputs(wl, 2, lengths=[5000, 4097, 129, 2048])
-    say(f"[case] chunk={chunk} kernel={kernel}")
+    say(f"[case] chunk={chunk} kernel={kernel} items={items}")
     dev = Device(s)
     rho = dev.probe()
     ref = oracle_out(s, oracle_rho(s))
-    with pb.options(chunk=chunk, kernel=kernel):
+    with pb.options(chunk=chunk, kernel=kernel, items=items):
         o32 = to64(dev.decode(rho, out_dtype=torch.float32))
     torch.cuda.synchronize()
     say(f"chunk={chunk} kernel={kernel}: rel {rel_l2(o32, ref):.3e} max_abs {max_abs(o32, ref):.3e}")
