@@ -1,7 +1,8 @@
 """Parallax decode benchmark on one MI355X.
 
 A step is one pass of the whole hot path over one batch: the probe
-rho = W_R x followed by the decode (split-K pass + merge) for every sequence.
+rho = W_R x, the decode split-K pass and the merge of the splits, for every
+sequence.
 The default workload is the mid-context GQA decode (B=16, Hq=16, Hkv=8, d=128,
 ctx=4096, d_model=2048, bf16 cache). Inputs are resident in HBM before timing;
 several independently seeded input sets are rotated so that every step reads
@@ -11,7 +12,7 @@ Output: one JSON line (metric, value = decode tokens/s, ms_per_step, roofline
 of the dominant kernel, CPU oracle baseline, ...).
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload 2]
-                    [--sets 3] [--no-cpu-baseline] [--sweep]
+                    [--sets 3] [--no-cpu-baseline] [--sweep] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -119,21 +120,28 @@ def run_workload(args, wl_id: int, emit: bool = True):
     torch.cuda.synchronize()
     print(f"# bench: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    pb.profile_reset()
+    # Timed region: K steps, nothing else on the stream.
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(pb, wl, dev_sets[i % len(dev_sets)])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    print(f"# bench: timed {args.steps} steps in {total_ms:.3f} ms", file=sys.stderr, flush=True)
+
+    # Same K steps again with per-launch HIP events (stamped by each kernel's
+    # dispatch on the launch stream) for the dominant kernel's duration.
+    pb.profile_reset()
     with pb.options(profile=1):
-        torch.cuda.synchronize()
-        ev0.record(stream)
         for i in range(args.steps):
             step(pb, wl, dev_sets[i % len(dev_sets)])
-        ev1.record(stream)
         torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
     dec_ms, dec_n = pb.profile_read(pb.KERNEL_DECODE)
     mrg_ms, mrg_n = pb.profile_read(pb.KERNEL_MERGE)
     prb_ms, prb_n = pb.profile_read(pb.KERNEL_PROBE)
-    print(f"# bench: timed {args.steps} steps in {total_ms:.3f} ms", file=sys.stderr, flush=True)
 
     ms_step = total_ms / args.steps
     # algorithmic bytes, averaged over the rotated sets
@@ -234,6 +242,9 @@ def main():
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 256 MiB device-to-device 3 times (a kernel of known "
+                         "traffic, to scale hardware byte counters)")
     ap.add_argument("--sweep-max-gib", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -245,6 +256,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.sweep:
         run_sweep(args)
         return

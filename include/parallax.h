@@ -42,7 +42,7 @@ typedef enum {
   PARALLAX_ERR_INVALID_ARG = 1,   /* bad size, null or misaligned pointer, Hq % Hkv != 0 */
   PARALLAX_ERR_UNSUPPORTED = 2,   /* valid but unsupported: d not in {64, 128}, unknown dtype */
   PARALLAX_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed */
-  PARALLAX_ERR_NO_MEMORY = 4      /* the split-K workspace could not be allocated */
+  PARALLAX_ERR_NO_MEMORY = 4      /* the split-K workspace could not be allocated or grown */
 } parallax_status;
 
 typedef enum {
@@ -93,10 +93,16 @@ int parallax_probe(const void* W_R, const void* x, float* rho,
  *
  * Requires B, Hq, Hkv, max_ctx >= 1, Hq % Hkv == 0, d in {64, 128}. A sequence
  * with seq_lens[b] == 0 gets out = 0 (a convention). seq_lens[b] > max_ctx is
- * clamped to max_ctx on the device (memory safety; a caller error). Long
- * sequences are split into chunks processed in parallel and merged by their
- * running maxima; the split-K workspace is allocated stream-ordered on
- * `stream` (hipMallocAsync / hipFreeAsync) and released by the same stream.
+ * clamped to max_ctx on the device (memory safety; a caller error).
+ *
+ * Long sequences are split into chunks processed in parallel and a second
+ * kernel merges the chunks' states by their running maxima (sequences that fit
+ * in one chunk are finished by the first kernel). The chunk states live in a
+ * workspace the library owns, cached per (device, stream) and kept until the
+ * process ends; it grows stream-ordered on `stream` (hipMallocAsync, old
+ * buffer hipFreeAsync'd). Growing is refused (PARALLAX_ERR_NO_MEMORY) while
+ * `stream` is being captured into a graph: make one call of the largest shape
+ * on that stream before capturing.
  */
 int parallax_decode(const void* q, const float* rho, const void* k_cache,
                     const void* v_cache, const int* seq_lens, void* out,
@@ -138,10 +144,12 @@ int parallax_set_option(int option, int value);
 int parallax_get_option(int option, int* value);
 
 /*
- * Kernel timing through HIP events recorded on the launch stream when
- * PARALLAX_OPT_PROFILE is 1. kernel: 0 = probe, 1 = decode (split-K pass),
- * 2 = merge. parallax_profile_read waits for the recorded events and returns
- * the summed duration (ms) and the number of launches since the last reset.
+ * Kernel timing when PARALLAX_OPT_PROFILE is 1: every launch carries start and
+ * stop HIP events stamped by its own dispatch (hipExtLaunchKernel), so the
+ * timing adds no work between kernels. kernel: 0 = probe, 1 = decode
+ * (split-K pass), 2 = merge.
+ * parallax_profile_read waits for the recorded events and returns the summed
+ * duration (ms) and the number of launches since the last reset.
  */
 int parallax_profile_read(int kernel, double* total_ms, long long* launches);
 int parallax_profile_reset(void);

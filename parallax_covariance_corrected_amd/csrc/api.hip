@@ -1,10 +1,13 @@
 // Host side of the libparallax C ABI (declared in include/parallax.h):
-// argument checks, the split-K plan, the stream-ordered workspace, kernel
+// argument checks, the split-K plan, the per-stream workspace, kernel
 // launches, error reporting and optional per-kernel event timing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <map>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/parallax.h"
@@ -32,6 +35,8 @@ int g_opt_profile = 0;
 int g_opt_items = 0;
 
 // ---------------------------------------------------------------- profiling
+// Start/stop events are handed to hipExtLaunchKernel, which stamps them from
+// the kernel's own dispatch packet (no extra packets between kernels).
 struct Timing {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
   double total_ms = 0.0;
@@ -52,30 +57,73 @@ hipEvent_t take_event() {
   return e;
 }
 
-// Records an event before a launch and, via finish(), after it.
-struct KernelTimer {
-  int kind;
-  hipStream_t stream;
-  hipEvent_t start = nullptr;
-  KernelTimer(int k, hipStream_t s) : kind(k), stream(s) {
-    if (!g_opt_profile) return;
-    std::lock_guard<std::mutex> g(g_prof_mu);
-    start = take_event();
-    if (start && hipEventRecord(start, stream) != hipSuccess) start = nullptr;
+parallax::LaunchEvents profile_events() {
+  parallax::LaunchEvents ev;
+  if (!g_opt_profile) return ev;
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  ev.start = take_event();
+  ev.stop = take_event();
+  if (!ev.start || !ev.stop) {
+    if (ev.start) g_event_pool.push_back(ev.start);
+    if (ev.stop) g_event_pool.push_back(ev.stop);
+    ev.start = ev.stop = nullptr;
   }
-  void finish() {
-    if (!start) return;
-    std::lock_guard<std::mutex> g(g_prof_mu);
-    hipEvent_t stop = take_event();
-    if (stop && hipEventRecord(stop, stream) == hipSuccess) {
-      g_prof[kind].pending.emplace_back(start, stop);
-    } else {
-      g_event_pool.push_back(start);
-      if (stop) g_event_pool.push_back(stop);
-    }
-    start = nullptr;
+  return ev;
+}
+
+void profile_record(int kind, parallax::LaunchEvents ev, bool launched) {
+  if (!ev.start) return;
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  if (launched) {
+    g_prof[kind].pending.emplace_back(ev.start, ev.stop);
+  } else {
+    g_event_pool.push_back(ev.start);
+    g_event_pool.push_back(ev.stop);
   }
+}
+
+// ---------------------------------------------------------------- workspace
+// Split-K partial states, cached per (device, stream): calls on one stream are
+// ordered, so they can share one buffer; calls on different streams never do.
+// A buffer only grows; growing is stream-ordered (allocate, then free the old
+// one on the same stream) and is refused while the stream is being captured
+// into a graph.
+struct Workspace {
+  void* base = nullptr;
+  size_t bytes = 0;
 };
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int get_workspace(hipStream_t stream, size_t bytes, void** base) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> g(g_ws_mu);
+  Workspace& w = g_ws[std::make_pair(dev, stream)];
+  if (w.base == nullptr || w.bytes < bytes) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cap != hipStreamCaptureStatusNone)
+      return fail(PARALLAX_ERR_NO_MEMORY,
+                  "the split-K workspace of this stream must grow, which cannot happen during "
+                  "graph capture: run one call of this size on the stream before capturing");
+    Workspace nw;
+    nw.bytes = round_up(std::max(bytes, w.bytes), 1 << 20);
+    e = hipMallocAsync(&nw.base, nw.bytes, stream);
+    if (e != hipSuccess || !nw.base) return fail(PARALLAX_ERR_NO_MEMORY, "workspace allocation failed");
+    if (w.base) {
+      e = hipFreeAsync(w.base, stream);
+      if (e != hipSuccess) return hip_fail(e, "hipFreeAsync");
+    }
+    w = nw;
+  }
+  *base = w.base;
+  return PARALLAX_OK;
+}
 
 // ---------------------------------------------------------------- planning
 struct Plan {
@@ -103,14 +151,18 @@ int check_decode_shape(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
   return PARALLAX_OK;
 }
 
+int head_block(int G, bool mfma) {
+  if (mfma) return G <= 4 ? G : (G % 4 == 0 ? 4 : (G % 3 == 0 ? 3 : (G % 2 == 0 ? 2 : 1)));
+  return (G % 4 == 0) ? 4 : (G % 3 == 0) ? 3 : (G % 2 == 0) ? 2 : 1;
+}
+
 Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
   Plan p;
   const int G = Hq / Hkv;
   const bool mfma_ok = dtype != PARALLAX_F32 && parallax::decode_mfma_supported(d, G);
   bool mfma = mfma_ok;
   if (g_opt_kernel == 1) mfma = false;
-  const int GH = G <= 4 ? G : (G % 4 == 0 ? 4 : (G % 3 == 0 ? 3 : (G % 2 == 0 ? 2 : 1)));
-  const long long units = (long long)B * Hkv * (mfma ? G / GH : 1);
+  const long long units = (long long)B * Hkv * (G / head_block(G, mfma));
   // Wave items (one wave per item) suit many short sequences; workgroup items
   // (four waves per item) suit long ones.
   bool wave_items = mfma && units >= 1024 && max_ctx <= 1024;
@@ -119,10 +171,12 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
   p.kernel = !mfma ? 1 : (wave_items ? 3 : 2);
   int chunk = g_opt_chunk;
   if (chunk <= 0) {
-    // Enough items to fill 256 compute units (2048 waves or 512 workgroups),
-    // chunks of 64 (wave items) / 128 (workgroup items) to 2048 keys so that a
-    // ragged batch stays balanced.
-    const long long target = wave_items ? 2048 : 512;
+    // About one busy workgroup per compute unit (256; 2048 waves for wave
+    // items): fewer, longer items amortise each item's prologue and epilogue,
+    // which measured faster than more, shorter ones. Chunks stay within
+    // 64 (wave items) / 128 (workgroup items) .. 2048 keys so that a ragged
+    // batch stays balanced.
+    const long long target = wave_items ? 2048 : 256;
     const long long want = units >= target ? 1 : (target + units - 1) / units;
     long long c = (max_ctx + want - 1) / want;
     c = (c + 63) / 64 * 64;
@@ -230,9 +284,9 @@ int parallax_probe(const void* W_R, const void* x, float* rho, int B, int Hq, in
   if ((long long)d_model * 2 * 64 >= (1LL << 30) || (long long)Hq * d > (1LL << 28) ||
       (long long)B > (1LL << 22))
     return fail(PARALLAX_ERR_UNSUPPORTED, "probe size out of range");
-  KernelTimer tm(0, stream);
-  hipError_t e = parallax::launch_probe(W_R, x, rho, B, Hq * d, d_model, f32 ? 1 : 0, stream);
-  tm.finish();
+  const parallax::LaunchEvents ev = profile_events();
+  hipError_t e = parallax::launch_probe(W_R, x, rho, B, Hq * d, d_model, f32 ? 1 : 0, ev, stream);
+  profile_record(0, ev, e == hipSuccess);
   if (e != hipSuccess) return hip_fail(e, "probe launch");
   return PARALLAX_OK;
 }
@@ -279,31 +333,25 @@ int parallax_decode(const void* q, const float* rho, const void* k_cache, const 
   a.out_f32 = (dtype == PARALLAX_BF16) ? 0 : 1;
   a.scale_log2 = parallax::kLog2e / sqrtf((float)d);
 
-  void* ws = nullptr;
   if (p.splits > 1) {
     const size_t states = (size_t)B * Hq * p.splits;
-    const size_t bytes = states * sizeof(float4) + states * 2 * d * sizeof(float);
-    hipError_t e = hipMallocAsync(&ws, bytes, stream);
-    if (e != hipSuccess || !ws) return fail(PARALLAX_ERR_NO_MEMORY, "split-K workspace allocation failed");
+    void* ws = nullptr;
+    rc = get_workspace(stream, states * sizeof(float4) + states * 2 * d * sizeof(float), &ws);
+    if (rc != PARALLAX_OK) return rc;
     a.ml = (float4*)ws;
     a.ap = (float*)((char*)ws + states * sizeof(float4));
   }
 
-  hipError_t e;
-  {
-    KernelTimer tm(1, stream);
-    e = (p.kernel >= 2) ? parallax::launch_decode_mfma(a, d, p.kernel == 3 ? 1 : 0, stream)
-                        : parallax::launch_decode_generic(a, d, dtype == PARALLAX_F32 ? 1 : 0, stream);
-    tm.finish();
-  }
+  parallax::LaunchEvents ev = profile_events();
+  hipError_t e =
+      (p.kernel >= 2)
+          ? parallax::launch_decode_mfma(a, d, p.kernel == 3 ? 1 : 0, ev, stream)
+          : parallax::launch_decode_generic(a, d, dtype == PARALLAX_F32 ? 1 : 0, ev, stream);
+  profile_record(1, ev, e == hipSuccess);
   if (e == hipSuccess && p.splits > 1) {
-    KernelTimer tm(2, stream);
-    e = parallax::launch_merge(a, d, stream);
-    tm.finish();
-  }
-  if (ws) {
-    hipError_t f = hipFreeAsync(ws, stream);
-    if (e == hipSuccess && f != hipSuccess) e = f;
+    ev = profile_events();
+    e = parallax::launch_merge(a, d, ev, stream);
+    profile_record(2, ev, e == hipSuccess);
   }
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return PARALLAX_OK;

@@ -2,6 +2,7 @@
 // gfx950 (CDNA4) only: 64-lane wavefronts, bf16 matrix cores, raw buffer loads.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -85,17 +86,34 @@ struct DecodeArgs {
   float* ap;
   int B, Hq, Hkv, max_ctx;
   int chunk;       // keys per split
-  int splits;      // splits per (sequence, KV head); 1 => write out directly
+  int splits;      // splits per (sequence, KV head)
   int out_f32;     // 1: out is fp32, 0: bf16
   float scale_log2;  // log2(e) / sqrt(d)
 };
 
+__device__ __forceinline__ void store_output(const DecodeArgs& a, size_t idx, float o) {
+  if (a.out_f32) store_out<float>((float*)a.out + idx, o);
+  else store_out<uint16_t>((uint16_t*)a.out + idx, o);
+}
+
+// A sequence that fits in one chunk (including length 0) is finished by its
+// split 0, which writes the output; longer ones leave one partial state per
+// non-empty split for the merge kernel.
+__device__ __forceinline__ bool single_chunk(const DecodeArgs& a, int n) { return n <= a.chunk; }
+
+// Optional start/stop events stamped by the dispatch packet (profiling).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // Internal launchers (one translation unit each). Return hipError_t.
-hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, hipStream_t s);
+hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, LaunchEvents ev,
+                                 hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, LaunchEvents ev,
+                              hipStream_t s);
+hipError_t launch_merge(const DecodeArgs& a, int d, LaunchEvents ev, hipStream_t s);
 bool decode_mfma_supported(int d, int G);
-hipError_t launch_merge(const DecodeArgs& a, int d, hipStream_t s);
 hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, int K,
-                        int f32_inputs, hipStream_t s);
+                        int f32_inputs, LaunchEvents ev, hipStream_t s);
 
 }  // namespace parallax

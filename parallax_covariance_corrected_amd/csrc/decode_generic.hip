@@ -1,11 +1,12 @@
 // Generic vector-ALU Parallax decode kernel (fp32 or bf16 storage, d in {64, 128},
 // any GQA group). Serves the fp32 path and cross-checks the matrix-core kernel.
 //
-// One workgroup (4 waves) per (sequence, KV head, head block, split). Each key
+// One workgroup (4 waves) per (split, sequence, KV head, head block). Each key
 // is read by LPK lanes with one 16-byte load of K and one of V; the lanes of a
 // key reduce the score s = q.k and the probe p = k.rho with xor shuffles and
 // keep their own exact online state (m, l, S, A, P). States are merged across
-// key groups (shuffles) and waves (LDS) by their running maxima. Both
+// key groups (shuffles) and waves (LDS) by their running maxima; the merge
+// kernel combines the splits of a long sequence. Both
 // branches read the same K/V rows (zubnet.ai (pt), "Parallax mantém softmax
 // ...", second paragraph: one KV stream feeds softmax and correction).
 #include "common.h"
@@ -58,15 +59,19 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
 
   const int G = a.Hq / a.Hkv;
   const int hblocks = G / GB;
-  int wg = blockIdx.x;
-  const int split = wg % a.splits; wg /= a.splits;
-  const int hb = wg % hblocks; wg /= hblocks;
-  const int kvh = wg % a.Hkv;
-  const int b = wg / a.Hkv;
+  // Split-major numbering: consecutive workgroups (dealt round-robin to the
+  // XCDs) take different sequences of the same split.
+  const int units = a.B * a.Hkv * hblocks;
+  const int split = blockIdx.x / units;
+  const int unit_id = blockIdx.x - split * units;
+  const int hb = unit_id % hblocks;
+  const int kvh = (unit_id / hblocks) % a.Hkv;
+  const int b = unit_id / hblocks / a.Hkv;
   const int n = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int c0 = split * a.chunk;
-  if (a.splits > 1 && c0 >= n) return;   // empty split: the merge never reads it
+  if (split > 0 && c0 >= n) return;   // empty split (split 0 always runs: n = 0 -> out = 0)
   const int c1 = min(c0 + a.chunk, n);
+  const bool direct = single_chunk(a, n);   // split 0 writes the output itself
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kg = lane / LPK, sub = lane % LPK;
@@ -160,10 +165,8 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
       At = fmaf(c, sA[w][h][i], At); Pt = fmaf(c, sP[w][h][i], Pt);
     }
     const size_t bh = (size_t)b * a.Hq + h0 + h;
-    if (a.splits == 1) {
-      const float o = parallax_out(At, Pt, lt, St);
-      if (a.out_f32) store_out<float>((float*)a.out + bh * D + i, o);
-      else store_out<uint16_t>((uint16_t*)a.out + bh * D + i, o);
+    if (direct) {
+      store_output(a, bh * D + i, parallax_out(At, Pt, lt, St));
     } else {
       const size_t ps = bh * a.splits + split;
       a.ap[ps * 2 * D + i] = At;
@@ -174,25 +177,27 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
 }
 
 template <bool F32IN, int D>
-hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_d(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int GB = (G % 4 == 0) ? 4 : (G % 3 == 0) ? 3 : (G % 2 == 0) ? 2 : 1;
   const size_t grid = (size_t)a.B * a.Hkv * (G / GB) * a.splits;
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid), blk(256);
   switch (GB) {
-    case 4: hipLaunchKernelGGL((decode_generic_kernel<F32IN, D, 4>), dim3(grid), dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_generic_kernel<F32IN, D, 3>), dim3(grid), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_generic_kernel<F32IN, D, 2>), dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_generic_kernel<F32IN, D, 1>), dim3(grid), dim3(256), 0, s, a); break;
+    case 4: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 4>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 3: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 3>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 2>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 1>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, hipStream_t s) {
-  if (f32_inputs) return d == 64 ? launch_d<true, 64>(a, s) : launch_d<true, 128>(a, s);
-  return d == 64 ? launch_d<false, 64>(a, s) : launch_d<false, 128>(a, s);
+hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, LaunchEvents ev,
+                                 hipStream_t s) {
+  if (f32_inputs) return d == 64 ? launch_d<true, 64>(a, ev, s) : launch_d<true, 128>(a, ev, s);
+  return d == 64 ? launch_d<false, 64>(a, ev, s) : launch_d<false, 128>(a, ev, s);
 }
 
 }  // namespace parallax

@@ -8,14 +8,18 @@
 // with both branches fed by one read of each K/V row (same paragraph: the KV
 // stream is shared, which is what doubles the arithmetic intensity).
 //
-// Work items. An item is (sequence, KV head, head block of GH query heads,
-// split of `chunk` keys). Two decompositions share the same tile code:
+// Work items. An item is (split of `chunk` keys, sequence, KV head, head block
+// of GH query heads), numbered split-major so that consecutive workgroups —
+// which the dispatcher deals round-robin to the 8 XCDs — take different
+// sequences of the same split: the non-empty items of a ragged or sparsely
+// filled cache then spread over every XCD. Two decompositions share the tile
+// code:
 //  * workgroup items (long contexts): the 4 waves of a workgroup take
 //    interleaved 16-key tiles of one item and merge their states in LDS;
-//  * wave items (short contexts, many sequences): every wave owns one item,
-//    so a workgroup serves 4 items with no cross-wave merge.
-// An item with one split writes the output; otherwise it writes its partial
-// state (m, l, S, A, P) for the merge kernel.
+//  * wave items (short contexts, many sequences): every wave owns one item.
+// A sequence that fits in one chunk gets its output written directly;
+// otherwise each non-empty split writes its partial state (m, l, S, A, P)
+// and the merge kernel combines them.
 //
 // Per wave, 16-key tiles stream through a 3-deep register ring: the loads of
 // tiles t+1 and t+2 are in flight while tile t is computed. K/V rows are read
@@ -29,18 +33,20 @@
 //    each head (exact: bf16 x bf16 products are exact in fp32) and rho of each
 //    head split as rho_hi + rho_lo (two bf16 operands accumulated into the same
 //    fp32 result, so rho keeps ~16 significant bits). Lane l receives keys
-//    4*(l/16) + r, r = 0..3, of column l % 16.
+//    4*(l/16) + r, r = 0..3, of column l % 16. X lives in LDS.
 //  * online softmax with a lazy rescale: the running max moves only when a
 //    score exceeds it by more than 8 (log2 units), so e <= 2^8 between
 //    rescales; the common path needs no cross-lane reduction.
 //  * weights: e for the score columns, e*p for the probe columns, moved next
 //    to each other with DPP lane moves inside 4- or 16-lane rows.
-//  * weighted value sums: fp32 4x4x1 MFMA blocks (16 blocks per instruction):
-//    A operand = the weight rows (e_h, e_h p_h) of one key, B operand = one
-//    value dim of that key, so weights stay fp32 (a bf16 weight would cost
-//    about 1e-3 relative error) and V needs no transpose: each lane's 16-byte
-//    V load supplies 8 consecutive dims.
+//  * weighted value sums: fp32 4x4x1 MFMA blocks with the A operand broadcast
+//    from one block (the weight rows (e_h, e_h p_h) of one key) to all 16
+//    blocks, whose B operands are 64 consecutive value dims of that key (one
+//    32-bit load of 2 bf16 dims per lane). Weights stay fp32 (a bf16 weight
+//    would cost about 1e-3 relative error), V needs no transpose, and each
+//    lane accumulates only its own dims.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -48,6 +54,9 @@ namespace parallax {
 namespace {
 
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
+// K/V rows are read exactly once: non-temporal loads keep them from displacing
+// reused lines in the caches.
+constexpr int kStreamLoad = 2;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -78,59 +87,85 @@ struct Layout {
 template <int D>
 struct KV {
   static constexpr int NC = D / 32;    // 32-dim chunks of the score product
-  static constexpr int EPV = D / 16;   // value dims per lane
+  static constexpr int TPL = D / 64;   // value dims per lane (per key)
   static constexpr int ROW = 2 * D;    // bytes per cache row
-  using VW = typename std::conditional<D == 128, u32x4, u32x2>::type;
+  using VE = typename std::conditional<D == 128, unsigned, unsigned short>::type;
   struct Tile {
     u32x4 k[NC];
-    VW v[4];
+    VE v[16];
   };
-  __device__ static VW vload(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    if constexpr (D == 128) return buf_load16(r, off);
-    else return buf_load8(r, off);
+  __device__ static VE vload(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    if constexpr (D == 128) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kStreamLoad);
+    else return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kStreamLoad);
   }
-  __device__ static float velem(const VW& w, int t) {
-    return (t & 1) ? bf16_hi(w[t >> 1]) : bf16_lo(w[t >> 1]);
+  __device__ static float velem(VE w, int t) {
+    if constexpr (D == 128) return t ? bf16_hi(w) : bf16_lo(w);
+    else return bf16_bits_to_f32(w);
   }
 };
+
+// Weighted value sums of key KK of a tile: broadcast block 4*(KK/4) (the lanes
+// holding that key's weight rows) to every block.
+template <int D, int NSET, int KK>
+__device__ __forceinline__ void pv_key(const typename KV<D>::Tile& tl, const float (&w0)[4],
+                                       const float (&w1)[4], f32x4 (&acc)[NSET][KV<D>::TPL]) {
+  constexpr int ABID = 4 * (KK >> 2), R = KK & 3;
+#pragma unroll
+  for (int t = 0; t < KV<D>::TPL; ++t) {
+    const float vf = KV<D>::velem(tl.v[KK], t);
+    acc[0][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w0[R], vf, acc[0][t], 4, ABID, 0);
+    if constexpr (NSET > 1)
+      acc[1][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w1[R], vf, acc[1][t], 4, ABID, 0);
+  }
+}
+template <int D, int NSET, int... KK>
+__device__ __forceinline__ void pv_tile(const typename KV<D>::Tile& tl, const float (&w0)[4],
+                                        const float (&w1)[4], f32x4 (&acc)[NSET][KV<D>::TPL],
+                                        std::integer_sequence<int, KK...>) {
+  (pv_key<D, NSET, KK>(tl, w0, w1, acc), ...);
+}
 
 template <int D, int GH, bool WAVE_ITEM>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   using L = Layout<GH>;
   using C = KV<D>;
-  constexpr int NC = C::NC, EPV = C::EPV, ROW = C::ROW, NSET = L::NSET;
+  constexpr int NC = C::NC, TPL = C::TPL, ROW = C::ROW, NSET = L::NSET;
   constexpr int STRIDE = WAVE_ITEM ? 16 : 64;   // keys between a wave's tiles
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = a.Hq / a.Hkv;
   const int hblocks = G / GH;
+  const int units = a.B * a.Hkv * hblocks;
   int item = WAVE_ITEM ? blockIdx.x * 4 + wave : blockIdx.x;
-  if (WAVE_ITEM && item >= a.B * a.Hkv * hblocks * a.splits) return;
-  const int split = item % a.splits; item /= a.splits;
-  const int hb = item % hblocks; item /= hblocks;
-  const int kvh = item % a.Hkv;
-  const int b = item / a.Hkv;
+  if (WAVE_ITEM && item >= units * a.splits) return;
+  const int split = item / units;
+  const int unit_id = item - split * units;
+  const int hb = unit_id % hblocks;
+  const int kvh = (unit_id / hblocks) % a.Hkv;
+  const int b = unit_id / hblocks / a.Hkv;
   const int n = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int c0 = split * a.chunk;
-  if (a.splits > 1 && c0 >= n) return;   // empty split: the merge never reads it
+  if (split > 0 && c0 >= n) return;   // empty split (split 0 always runs: n = 0 -> out = 0)
   const int c1 = min(c0 + a.chunk, n);
+  const bool direct = single_chunk(a, n);   // split 0 writes the output itself
 
-  const int l16 = lane & 15, grp = lane >> 4, quad = l16 >> 2, qi = lane & 3;
+  const int grp = lane >> 4, quad = (lane & 15) >> 2, qi = lane & 3;
   const int h0 = kvh * G + hb * GH;
 
   // K/V streams of this (sequence, KV head), ranged to [0, c1).
   const size_t seq = ((size_t)b * a.Hkv + kvh) * (size_t)a.max_ctx;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc((const char*)a.k + seq * ROW, (unsigned)c1 * ROW);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const char*)a.v + seq * ROW, (unsigned)c1 * ROW);
-  const unsigned koff = l16 * ROW + 16 * grp;
-  const unsigned voff = 4 * grp * ROW + l16 * (ROW / 16);
+  const unsigned koff = (lane & 15) * ROW + 16 * grp;
+  const unsigned voff = lane * (ROW / 64);
   auto load = [&](typename C::Tile& t, int j) {
     const unsigned base = (unsigned)j * ROW;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) t.k[c] = buf_load16(krs, base + koff + 64 * c);
+    for (int c = 0; c < NC; ++c)
+      t.k[c] = __builtin_amdgcn_raw_buffer_load_b128(krs, base + koff + 64 * c, 0, kStreamLoad);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) t.v[c] = C::vload(vrs, base + voff + c * ROW);
+    for (int kk = 0; kk < 16; ++kk) t.v[kk] = C::vload(vrs, base + voff + kk * ROW);
   };
 
   // Start streaming before the q/rho prologue so the latencies overlap.
@@ -153,8 +188,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   }
 
   // B operands: column vector (q, or rho split hi + lo) at dims 32c + 8*grp + t,
-  // staged in this wave's LDS slot and re-read per tile (keeps VGPRs free for
-  // loads in flight).
+  // staged in this wave's LDS slot and re-read per tile.
   __shared__ u32x4 sB[4][2][NC][64];
   {
     const size_t bh = (size_t)b * a.Hq + h0 + chead;
@@ -181,11 +215,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
   float m_run = kNegInf;      // running max (log2 domain), score lanes
   float lsum = 0.f, ssum = 0.f;
-  f32x4 acc[NSET][EPV];
+  f32x4 acc[NSET][TPL];
 #pragma unroll
   for (int s = 0; s < NSET; ++s)
 #pragma unroll
-    for (int t = 0; t < EPV; ++t) acc[s][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < TPL; ++t) acc[s][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const typename C::Tile& tl, int jt) {
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -228,7 +262,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
           const int h = L::head(s, r);
           if (h < 0) continue;
 #pragma unroll
-          for (int t = 0; t < EPV; ++t) acc[s][t][r] *= ah[h];
+          for (int t = 0; t < TPL; ++t) acc[s][t][r] *= ah[h];
         }
       float a0 = 1.f, a1 = 1.f;
 #pragma unroll
@@ -247,6 +281,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         constexpr int kQuadPerm = GH == 2 ? 0x44 : 0x00;   // lane qi reads lane qi - GH
         const float esrc = dpp<kQuadPerm>(e);
         w0[r] = is_s ? e : (is_p ? esrc * sacc[r] : 0.f);
+        w1[r] = 0.f;
         lsum += w0[r];
       } else {
         const float efrom = dpp<kDppRowShr8>(e);
@@ -258,16 +293,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         ssum += w1[r];
       }
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int t = 0; t < EPV; ++t) {
-        const float vf = C::velem(tl.v[c], t);
-        acc[0][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w0[c], vf, acc[0][t], 0, 0, 0);
-        if constexpr (NSET > 1)
-          acc[1][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w1[c], vf, acc[1][t], 0, 0, 0);
-      }
-    }
+    pv_tile<D, NSET>(tl, w0, w1, acc, std::make_integer_sequence<int, 16>{});
   };
 
   // Three-deep ring: compute tile t while tiles t+1, t+2 are loading.
@@ -285,27 +311,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     j += STRIDE;
   }
 
-  // Sum the four key slots (lane groups of 16) of this wave.
+  // Sum the per-lane weight sums over the four key slots (lane groups of 16).
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   if constexpr (NSET > 1) {
     ssum += __shfl_xor(ssum, 16);
     ssum += __shfl_xor(ssum, 32);
   }
-#pragma unroll
-  for (int s = 0; s < NSET; ++s)
-#pragma unroll
-    for (int t = 0; t < EPV; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = acc[s][t][r];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[s][t][r] = v;
-      }
-
+  // Lane l holds A and P of every head of the block at dims TPL*l + t.
   if constexpr (WAVE_ITEM) {
-    // This wave holds the whole item: per-head m, l, S from the score lanes.
     float mh[GH], lh[GH], sh[GH];
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
@@ -313,59 +327,53 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       lh[h] = readlane_f(lsum, h);
       sh[h] = (GH <= 2) ? readlane_f(lsum, GH + h) : readlane_f(ssum, h);
     }
-    if (grp == 0) {
 #pragma unroll
-      for (int h = 0; h < GH; ++h) {
-        const size_t bh = (size_t)b * a.Hq + h0 + h;
+    for (int h = 0; h < GH; ++h) {
+      const size_t bh = (size_t)b * a.Hq + h0 + h;
 #pragma unroll
-        for (int t = 0; t < EPV; ++t) {
-          float Av = 0.f, Pv = 0.f;
+      for (int t = 0; t < TPL; ++t) {
+        float Av = 0.f, Pv = 0.f;
 #pragma unroll
-          for (int s = 0; s < NSET; ++s)
+        for (int s = 0; s < NSET; ++s)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (L::head(s, r) != h) continue;
-              if (L::is_A(s, r)) Av = acc[s][t][r];
-              else Pv = acc[s][t][r];
-            }
-          const int i = l16 * EPV + t;
-          if (a.splits == 1) {
-            const float o = parallax_out(Av, Pv, lh[h], sh[h]);
-            if (a.out_f32) store_out<float>((float*)a.out + bh * D + i, o);
-            else store_out<uint16_t>((uint16_t*)a.out + bh * D + i, o);
-          } else {
-            const size_t ps = bh * a.splits + split;
-            a.ap[ps * 2 * D + i] = Av;
-            a.ap[ps * 2 * D + D + i] = Pv;
+          for (int r = 0; r < 4; ++r) {
+            if (L::head(s, r) != h) continue;
+            if (L::is_A(s, r)) Av = acc[s][t][r];
+            else Pv = acc[s][t][r];
           }
+        const int i = TPL * lane + t;
+        if (direct) {
+          store_output(a, bh * D + i, parallax_out(Av, Pv, lh[h], sh[h]));
+        } else {
+          const size_t ps = bh * a.splits + split;
+          a.ap[ps * 2 * D + i] = Av;
+          a.ap[ps * 2 * D + D + i] = Pv;
         }
-        if (a.splits > 1 && l16 == 0)
-          a.ml[bh * a.splits + split] = make_float4(mh[h], lh[h], sh[h], 0.f);
       }
+      if (!direct && lane == 0)
+        a.ml[bh * a.splits + split] = make_float4(mh[h], lh[h], sh[h], 0.f);
     }
     return;
   } else {
     __shared__ float sA[4][GH][D], sP[4][GH][D], sM[4][GH], sL[4][GH], sS[4][GH];
-    if (grp == 0) {
 #pragma unroll
-      for (int s = 0; s < NSET; ++s)
+    for (int s = 0; s < NSET; ++s)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int h = L::head(s, r);
-          if (h < 0) continue;
+      for (int r = 0; r < 4; ++r) {
+        const int h = L::head(s, r);
+        if (h < 0) continue;
 #pragma unroll
-          for (int t = 0; t < EPV; ++t) {
-            if (L::is_A(s, r)) sA[wave][h][l16 * EPV + t] = acc[s][t][r];
-            else sP[wave][h][l16 * EPV + t] = acc[s][t][r];
-          }
+        for (int t = 0; t < TPL; ++t) {
+          if (L::is_A(s, r)) sA[wave][h][TPL * lane + t] = acc[s][t][r];
+          else sP[wave][h][TPL * lane + t] = acc[s][t][r];
         }
-      if (lane < GH) sM[wave][lane] = m_run;
-      if constexpr (GH <= 2) {
-        if (lane < GH) sL[wave][lane] = lsum;
-        else if (lane < 2 * GH) sS[wave][lane - GH] = lsum;
-      } else {
-        if (lane < GH) { sL[wave][lane] = lsum; sS[wave][lane] = ssum; }
       }
+    if (lane < GH) sM[wave][lane] = m_run;
+    if constexpr (GH <= 2) {
+      if (lane < GH) sL[wave][lane] = lsum;
+      else if (lane < 2 * GH) sS[wave][lane - GH] = lsum;
+    } else {
+      if (lane < GH) { sL[wave][lane] = lsum; sS[wave][lane] = ssum; }
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < GH * D; idx += 256) {
@@ -381,10 +389,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         At = fmaf(c, sA[w][h][i], At); Pt = fmaf(c, sP[w][h][i], Pt);
       }
       const size_t bh = (size_t)b * a.Hq + h0 + h;
-      if (a.splits == 1) {
-        const float o = parallax_out(At, Pt, lt, St);
-        if (a.out_f32) store_out<float>((float*)a.out + bh * D + i, o);
-        else store_out<uint16_t>((uint16_t*)a.out + bh * D + i, o);
+      if (direct) {
+        store_output(a, bh * D + i, parallax_out(At, Pt, lt, St));
       } else {
         const size_t ps = bh * a.splits + split;
         a.ap[ps * 2 * D + i] = At;
@@ -404,17 +410,18 @@ int head_block(int G) {
 }
 
 template <int D, bool WI>
-hipError_t launch_dw(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int GH = head_block(G);
   const size_t items = (size_t)a.B * a.Hkv * (G / GH) * a.splits;
   const size_t grid = WI ? (items + 3) / 4 : items;
   if (grid > 0x7fffffffu || items > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid), blk(256);
   switch (GH) {
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4, WI>), dim3(grid), dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<D, 3, WI>), dim3(grid), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<D, 2, WI>), dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_mfma_kernel<D, 1, WI>), dim3(grid), dim3(256), 0, s, a); break;
+    case 4: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 4, WI>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 3: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 3, WI>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 2, WI>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 1, WI>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
   }
   return hipGetLastError();
 }
@@ -423,9 +430,10 @@ hipError_t launch_dw(const DecodeArgs& a, hipStream_t s) {
 
 bool decode_mfma_supported(int d, int G) { return (d == 64 || d == 128) && G >= 1; }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, hipStream_t s) {
-  if (wave_items) return d == 64 ? launch_dw<64, true>(a, s) : launch_dw<128, true>(a, s);
-  return d == 64 ? launch_dw<64, false>(a, s) : launch_dw<128, false>(a, s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, LaunchEvents ev,
+                              hipStream_t s) {
+  if (wave_items) return d == 64 ? launch_dw<64, true>(a, ev, s) : launch_dw<128, true>(a, ev, s);
+  return d == 64 ? launch_dw<64, false>(a, ev, s) : launch_dw<128, false>(a, ev, s);
 }
 
 }  // namespace parallax

@@ -6,7 +6,8 @@
 // the epilogue out = A/l - (P/l - (A/l)(S/l)), i.e. softmax attention minus the
 // softmax-weighted KV covariance times the probe (zubnet.ai (pt), "Parallax
 // mantém softmax ...", second paragraph). Only the splits that cover
-// [0, seq_lens[b]) are read; a sequence of length 0 gets out = 0.
+// [0, seq_lens[b]) are read; sequences that fit in one chunk (length 0
+// included) were finished by the decode kernel and are skipped.
 //
 // One workgroup per (sequence, query head): its 4 waves take interleaved
 // splits (loads of several splits in flight per wave), lanes own D/64 dims,
@@ -23,6 +24,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   const size_t bh = blockIdx.x;
   const int b = (int)(bh / a.Hq);
   const int n = min(max(a.seq_lens[b], 0), a.max_ctx);
+  if (single_chunk(a, n)) return;   // written by the decode kernel
   const int ns = (n + a.chunk - 1) / a.chunk;
   const float4* ml = a.ml + bh * a.splits;
   const float* ap = a.ap + bh * a.splits * 2 * D;
@@ -69,20 +71,18 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
       const int i = lane * DPL + k;
       const float At = sacc[0][i] + sacc[1][i] + sacc[2][i] + sacc[3][i];
       const float Pt = sacc[0][D + i] + sacc[1][D + i] + sacc[2][D + i] + sacc[3][D + i];
-      const float o = parallax_out(At, Pt, lt, St);
-      if (a.out_f32) store_out<float>((float*)a.out + bh * D + i, o);
-      else store_out<uint16_t>((uint16_t*)a.out + bh * D + i, o);
+      store_output(a, bh * D + i, parallax_out(At, Pt, lt, St));
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_merge(const DecodeArgs& a, int d, hipStream_t s) {
+hipError_t launch_merge(const DecodeArgs& a, int d, LaunchEvents ev, hipStream_t s) {
   const size_t grid = (size_t)a.B * a.Hq;
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  if (d == 64) hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+  if (d == 64) hipExtLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, ev.start, ev.stop, 0, a);
+  else hipExtLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 

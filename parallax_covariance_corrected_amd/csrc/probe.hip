@@ -112,28 +112,28 @@ __global__ __launch_bounds__(256) void probe_f32_kernel(const float* __restrict_
 }  // namespace
 
 hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, int K,
-                        int f32_inputs, hipStream_t s) {
+                        int f32_inputs, LaunchEvents ev, hipStream_t s) {
   if (f32_inputs) {
     const size_t total = (size_t)B * N;
     const size_t grid = (total + 255) / 256;
     if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(probe_f32_kernel, dim3(grid), dim3(256), 0, s, (const float*)W,
-                       (const float*)x, rho, B, N, K);
+    hipExtLaunchKernelGGL(probe_f32_kernel, dim3(grid), dim3(256), 0, s, ev.start, ev.stop, 0,
+                          (const float*)W, (const float*)x, rho, B, N, K);
     return hipGetLastError();
   }
   const uint16_t* Wb = (const uint16_t*)W;
   const uint16_t* xb = (const uint16_t*)x;
   if (B > 64) {
     dim3 grid((N + 63) / 64, (B + 63) / 64);
-    hipLaunchKernelGGL((probe_mfma_kernel<4, 4, 4, 2>), grid, dim3(256), 0, s, Wb, xb, rho, B, N, K);
+    hipExtLaunchKernelGGL((probe_mfma_kernel<4, 4, 4, 2>), grid, dim3(256), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
   } else {
     const int mt = (B + 15) / 16;
     dim3 grid((N + 15) / 16, 1);
     switch (mt) {
-      case 1: hipLaunchKernelGGL((probe_mfma_kernel<1, 1, 8, 8>), grid, dim3(512), 0, s, Wb, xb, rho, B, N, K); break;
-      case 2: hipLaunchKernelGGL((probe_mfma_kernel<2, 1, 8, 4>), grid, dim3(512), 0, s, Wb, xb, rho, B, N, K); break;
-      case 3: hipLaunchKernelGGL((probe_mfma_kernel<3, 1, 8, 4>), grid, dim3(512), 0, s, Wb, xb, rho, B, N, K); break;
-      default: hipLaunchKernelGGL((probe_mfma_kernel<4, 1, 8, 4>), grid, dim3(512), 0, s, Wb, xb, rho, B, N, K); break;
+      case 1: hipExtLaunchKernelGGL((probe_mfma_kernel<1, 1, 8, 8>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K); break;
+      case 2: hipExtLaunchKernelGGL((probe_mfma_kernel<2, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K); break;
+      case 3: hipExtLaunchKernelGGL((probe_mfma_kernel<3, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K); break;
+      default: hipExtLaunchKernelGGL((probe_mfma_kernel<4, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K); break;
     }
   }
   return hipGetLastError();

@@ -86,9 +86,9 @@ def test_plan_covers_context_and_picks_kernels():
     # many short sequences: one wave per item; long ones: four waves per item
     assert pb.decode_plan(2048, 16, 8, 128, 128)[2] == 3
     assert pb.decode_plan(16, 16, 8, 128, 4096)[2] == 2
-    # enough workgroups for 256 compute units on the mid-context workload
+    # about one workgroup per compute unit on the mid-context workload
     chunk, splits, _ = pb.decode_plan(16, 16, 8, 128, 4096)
-    assert 16 * 8 * splits >= 512
+    assert 16 * 8 * splits >= 256
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -202,6 +202,28 @@ def test_bitwise_repeatable_and_output_guards():
     assert torch.all(buf[:guard] == 12345.0) and torch.all(buf[guard + n:] == 12345.0)
 
 
+def test_workspace_grows_across_shapes_and_streams():
+    """The per-stream split-K workspace grows when a larger shape arrives and
+    its arrival counters return to zero after every call (smaller shapes after
+    larger ones, a second stream, repeated calls)."""
+    cases = [(2, 900, [900, 700]), (5, 4000, [4000, 3999, 2500, 1, 130]), (3, 1500, [1500, 20, 1499])]
+    side = torch.cuda.Stream()
+    for rep in range(2):
+        for B, ctx, lens in cases:
+            wl = WORKLOADS[2].scaled(B=B, ctx=ctx, d_model=64)
+            s = make_inputs(wl, 10 + B, lengths=lens)
+            say(f"[case] workspace B={B} ctx={ctx} rep={rep}")
+            dev = Device(s)
+            rho = dev.probe()
+            torch.cuda.synchronize()   # inputs ready before the side stream reads them
+            ref = oracle_out(s, oracle_rho(s))
+            for st in (torch.cuda.current_stream(), side):
+                with torch.cuda.stream(st):
+                    o = dev.decode(rho, out_dtype=torch.float32)
+                st.synchronize()
+                assert rel_l2(to64(o), ref) <= 1e-5
+
+
 @pytest.mark.parametrize("B,d_model,dtype", [(1, 2048, "bf16"), (17, 2560, "bf16"), (64, 2048, "bf16"),
                                              (65, 512, "bf16"), (130, 72, "bf16"), (3, 100, "f32")])
 def test_probe_shapes(B, d_model, dtype):
