@@ -215,6 +215,7 @@ int parallax_set_option(int option, int value) {
       if (value < 0 || value > 2) return fail(PARALLAX_ERR_INVALID_ARG, "items must be 0, 1 or 2");
       g_opt_items = value;
       return PARALLAX_OK;
+
     default:
       return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
   }

@@ -125,19 +125,19 @@ __device__ __forceinline__ void pv_tile(const typename KV<D>::Tile& tl, const fl
   (pv_key<D, NSET, KK>(tl, w0, w1, acc), ...);
 }
 
-template <int D, int GH, bool WAVE_ITEM>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+template <int D, int GH, bool WAVE_ITEM, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   using L = Layout<GH>;
   using C = KV<D>;
   constexpr int NC = C::NC, TPL = C::TPL, ROW = C::ROW, NSET = L::NSET;
-  constexpr int STRIDE = WAVE_ITEM ? 16 : 64;   // keys between a wave's tiles
+  constexpr int STRIDE = WAVE_ITEM ? 16 : 16 * NW;   // keys between a wave's tiles
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = a.Hq / a.Hkv;
   const int hblocks = G / GH;
   const int units = a.B * a.Hkv * hblocks;
-  int item = WAVE_ITEM ? blockIdx.x * 4 + wave : blockIdx.x;
+  int item = WAVE_ITEM ? blockIdx.x * NW + wave : blockIdx.x;
   if (WAVE_ITEM && item >= units * a.splits) return;
   const int split = item / units;
   const int unit_id = item - split * units;
@@ -188,9 +188,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   }
 
   // B operands: column vector (q, or rho split hi + lo) at dims 32c + 8*grp + t,
-  // staged in this wave's LDS slot and re-read per tile.
-  __shared__ u32x4 sB[4][2][NC][64];
-  {
+  // staged in LDS and re-read per tile: one copy per wave for wave items, one
+  // per workgroup (written by wave 0) for workgroup items.
+  constexpr int NBS = WAVE_ITEM ? NW : 1;
+  const int bslot = WAVE_ITEM ? wave : 0;
+  __shared__ u32x4 sB[NBS][2][NC][64];
+  if (WAVE_ITEM || wave == 0) {
     const size_t bh = (size_t)b * a.Hq + h0 + chead;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -208,10 +211,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
           lo[w] = pack_bf16x2(r[2 * w] - bf16_lo(hi[w]), r[2 * w + 1] - bf16_hi(hi[w]));
         }
       }
-      sB[wave][0][c][lane] = hi;
-      sB[wave][1][c][lane] = lo;
+      sB[bslot][0][c][lane] = hi;
+      sB[bslot][1][c][lane] = lo;
     }
   }
+  if constexpr (!WAVE_ITEM) __syncthreads();
 
   float m_run = kNegInf;      // running max (log2 domain), score lanes
   float lsum = 0.f, ssum = 0.f;
@@ -225,8 +229,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const bf16x8 bhi = as_bf16x8(sB[wave][0][c][lane]);
-      const bf16x8 blo = as_bf16x8(sB[wave][1][c][lane]);
+      const bf16x8 bhi = as_bf16x8(sB[bslot][0][c][lane]);
+      const bf16x8 blo = as_bf16x8(sB[bslot][1][c][lane]);
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[c]), bhi, sacc, 0, 0, 0);
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[c]), blo, sacc, 0, 0, 0);
     }
@@ -296,7 +300,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     pv_tile<D, NSET>(tl, w0, w1, acc, std::make_integer_sequence<int, 16>{});
   };
 
-  // Three-deep ring: compute tile t while tiles t+1, t+2 are loading.
+  // Three-deep ring: compute tile t while tiles t+1, t+2 are loading (deeper
+  // rings and 8-wave workgroups measured slower).
   while (j < c1) {
     load(t2, j + 2 * STRIDE);
     compute(t0, j);
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
     return;
   } else {
-    __shared__ float sA[4][GH][D], sP[4][GH][D], sM[4][GH], sL[4][GH], sS[4][GH];
+    __shared__ float sA[NW][GH][D], sP[NW][GH][D], sM[NW][GH], sL[NW][GH], sS[NW][GH];
 #pragma unroll
     for (int s = 0; s < NSET; ++s)
 #pragma unroll
@@ -376,14 +381,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       if (lane < GH) { sL[wave][lane] = lsum; sS[wave][lane] = ssum; }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < GH * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < GH * D; idx += NW * 64) {
       const int h = idx / D, i = idx % D;
       float M = sM[0][h];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) M = fmaxf(M, sM[w][h]);
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, sM[w][h]);
       float lt = 0.f, St = 0.f, At = 0.f, Pt = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float c = rescale(sM[w][h], M);
         lt = fmaf(c, sL[w][h], lt); St = fmaf(c, sS[w][h], St);
         At = fmaf(c, sA[w][h][i], At); Pt = fmaf(c, sP[w][h][i], Pt);
@@ -409,19 +414,19 @@ int head_block(int G) {
   return 1;
 }
 
-template <int D, bool WI>
+template <int D, bool WI, int NW>
 hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int GH = head_block(G);
   const size_t items = (size_t)a.B * a.Hkv * (G / GH) * a.splits;
-  const size_t grid = WI ? (items + 3) / 4 : items;
+  const size_t grid = WI ? (items + NW - 1) / NW : items;
   if (grid > 0x7fffffffu || items > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  const dim3 g((unsigned)grid), blk(256);
+  const dim3 g((unsigned)grid), blk(NW * 64);
   switch (GH) {
-    case 4: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 4, WI>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 3: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 3, WI>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 2, WI>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 1, WI>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 4, WI, NW>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 3: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 3, WI, NW>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 2, WI, NW>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 1, WI, NW>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
   }
   return hipGetLastError();
 }
@@ -432,8 +437,8 @@ bool decode_mfma_supported(int d, int G) { return (d == 64 || d == 128) && G >= 
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, LaunchEvents ev,
                               hipStream_t s) {
-  if (wave_items) return d == 64 ? launch_dw<64, true>(a, ev, s) : launch_dw<128, true>(a, ev, s);
-  return d == 64 ? launch_dw<64, false>(a, ev, s) : launch_dw<128, false>(a, ev, s);
+  if (wave_items) return d == 64 ? launch_dw<64, true, 4>(a, ev, s) : launch_dw<128, true, 4>(a, ev, s);
+  return d == 64 ? launch_dw<64, false, 4>(a, ev, s) : launch_dw<128, false, 4>(a, ev, s);
 }
 
 }  // namespace parallax
