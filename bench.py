@@ -101,6 +101,47 @@ def cpu_baseline(s, budget_s: float = 12.0):
                       f"scaled to the full step"}
 
 
+def matched_ratios(pb, wl, dev_sets, reps: int):
+    """Decode-only time of Parallax against plain softmax attention run by the
+    same kernel without the correction branch: at the same KV bytes
+    (I/O-matched: same heads) and at the same arithmetic (compute-matched:
+    twice the query heads over the same cache). Speed-up = softmax time /
+    Parallax time, so values above 1 mean Parallax is faster."""
+    import torch
+    q2 = [d["q"].repeat_interleave(2, dim=1).contiguous() for d in dev_sets]
+    out2 = torch.empty_like(q2[0])
+
+    def timed(fn):
+        for i in range(5):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def par(i):
+        d = dev_sets[i % len(dev_sets)]
+        pb.decode(d["q"], d["rho"], d["K"], d["V"], d["seq_lens"], out=d["out"])
+
+    def soft(i):
+        d = dev_sets[i % len(dev_sets)]
+        pb.softmax_decode(d["q"], d["K"], d["V"], d["seq_lens"], out=d["out"])
+
+    def soft2(i):
+        d = dev_sets[i % len(dev_sets)]
+        pb.softmax_decode(q2[i % len(dev_sets)], d["K"], d["V"], d["seq_lens"], out=out2)
+
+    t_par, t_soft, t_soft2 = timed(par), timed(soft), timed(soft2)
+    return {"parallax_decode_us": round(t_par, 3), "softmax_decode_us": round(t_soft, 3),
+            "softmax_2x_heads_decode_us": round(t_soft2, 3),
+            "io_matched_speedup": round(t_soft / t_par, 4),
+            "compute_matched_speedup": round(t_soft2 / t_par, 4)}
+
+
 def run_workload(args, wl_id: int, emit: bool = True):
     import torch
     from parallax_covariance_corrected_amd import binding as pb
@@ -180,6 +221,8 @@ def run_workload(args, wl_id: int, emit: bool = True):
                      "probe_avg_us": round(prb_ms / max(prb_n, 1) * 1e3, 3)},
         "cpu_baseline": None,
     }
+    if wl.dtype == "bf16":
+        rec["matched"] = matched_ratios(pb, wl, dev_sets, args.steps)
     if args.cpu_baseline:
         print("# bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(sets_host[0])

@@ -109,6 +109,19 @@ int parallax_decode(const void* q, const float* rho, const void* k_cache,
                     int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
                     hipStream_t stream);
 
+/*
+ * parallax_softmax_decode — the same decode kernel without the correction
+ * branch: plain softmax attention out[b][h] = sum_j w_j V[b][g][j], which is
+ * what Parallax reduces to when W_R = 0 (encorp.ai (de), section "Parallax
+ * behält Softmax bei"). It reads the same KV stream and does half the
+ * arithmetic per key, so timing it beside parallax_decode gives the cost of
+ * the correction at equal bytes (and, with twice the query heads, at equal
+ * arithmetic). Arguments, layouts and errors as parallax_decode, without rho.
+ */
+int parallax_softmax_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int* seq_lens, void* out, int B, int Hq, int Hkv, int d,
+                            int max_ctx, int dtype, hipStream_t stream);
+
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char* parallax_last_error(void);
 

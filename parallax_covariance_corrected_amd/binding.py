@@ -42,6 +42,7 @@ def lib() -> ctypes.CDLL:
         vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         L.parallax_probe.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
         L.parallax_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        L.parallax_softmax_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
         L.parallax_decode_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i),
                                            ctypes.POINTER(i), ctypes.POINTER(i)]
         L.parallax_set_option.argtypes = [i, i]
@@ -49,7 +50,8 @@ def lib() -> ctypes.CDLL:
         L.parallax_profile_read.argtypes = [i, ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_longlong)]
         L.parallax_profile_reset.argtypes = []
-        for name in ("parallax_probe", "parallax_decode", "parallax_decode_plan",
+        for name in ("parallax_probe", "parallax_decode", "parallax_softmax_decode",
+                     "parallax_decode_plan",
                      "parallax_set_option", "parallax_get_option", "parallax_profile_read",
                      "parallax_profile_reset"):
             getattr(L, name).restype = i
@@ -131,6 +133,28 @@ def decode(q: torch.Tensor, rho: torch.Tensor, k_cache: torch.Tensor, v_cache: t
     _check(lib().parallax_decode(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache),
                                  _ptr(seq_lens), _ptr(out), B, Hq, Hkv, d, max_ctx, code,
                                  _stream()))
+    return out
+
+
+def softmax_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   seq_lens: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """Plain softmax attention decode (the same kernel without the correction
+    branch): out[B, Hq, d] from q, k_cache/v_cache [B, Hkv, max_ctx, d], seq_lens."""
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _need(t, nm)
+    B, Hq, d = q.shape
+    _, Hkv, max_ctx, _ = k_cache.shape
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, k_cache and v_cache must share a dtype")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out")
+    code = _dtype_code(q.dtype, out.dtype)
+    _check(lib().parallax_softmax_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                         _ptr(out), B, Hq, Hkv, d, max_ctx, code, _stream()))
     return out
 
 

@@ -304,15 +304,20 @@ int parallax_decode_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype, 
   return PARALLAX_OK;
 }
 
-int parallax_decode(const void* q, const float* rho, const void* k_cache, const void* v_cache,
-                    const int* seq_lens, void* out, int B, int Hq, int Hkv, int d, int max_ctx,
-                    int dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by parallax_decode and parallax_softmax_decode (rho == nullptr).
+int decode_impl(const void* q, const float* rho, const void* k_cache, const void* v_cache,
+                const int* seq_lens, void* out, int B, int Hq, int Hkv, int d, int max_ctx,
+                int dtype, hipStream_t stream) {
   int rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
   if (rc != PARALLAX_OK) return rc;
-  if (!q || !rho || !k_cache || !v_cache || !seq_lens || !out)
+  if (!q || !k_cache || !v_cache || !seq_lens || !out)
     return fail(PARALLAX_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned(q, 16) || !aligned(rho, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(out, 16) || !aligned(seq_lens, 4))
+  if (!aligned(q, 16) || (rho && !aligned(rho, 16)) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(out, 16) || !aligned(seq_lens, 4))
     return fail(PARALLAX_ERR_INVALID_ARG, "pointers must be 16-byte aligned (seq_lens 4-byte)");
 
   const Plan p = make_plan(B, Hq, Hkv, d, max_ctx, dtype);
@@ -356,6 +361,25 @@ int parallax_decode(const void* q, const float* rho, const void* k_cache, const 
   }
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return PARALLAX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int parallax_decode(const void* q, const float* rho, const void* k_cache, const void* v_cache,
+                    const int* seq_lens, void* out, int B, int Hq, int Hkv, int d, int max_ctx,
+                    int dtype, hipStream_t stream) {
+  if (!rho) return fail(PARALLAX_ERR_INVALID_ARG, "null pointer argument (rho)");
+  return decode_impl(q, rho, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, d, max_ctx, dtype,
+                     stream);
+}
+
+int parallax_softmax_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int* seq_lens, void* out, int B, int Hq, int Hkv, int d,
+                            int max_ctx, int dtype, hipStream_t stream) {
+  return decode_impl(q, nullptr, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, d, max_ctx, dtype,
+                     stream);
 }
 
 }  // extern "C"

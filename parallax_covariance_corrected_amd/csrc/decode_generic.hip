@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
     const u32x4 qw = *(const u32x4*)((const char*)a.q + base * E::kSize);
     E::unpack(qw, qf[h]);
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) rf[h][i] = a.rho[base + i];
+    for (int i = 0; i < EPL; ++i) rf[h][i] = a.rho ? a.rho[base + i] : 0.f;   // no rho: softmax only
   }
 
   float m[GB], l[GB], S[GB], A[GB][EPL], P[GB][EPL];

@@ -31,14 +31,14 @@
 //  * scores and probes: one bf16 16x16x32 MFMA product K_tile (16 keys x 32
 //    dims) . X^T (32 dims x 16 columns) per 32 dims; the columns of X are q of
 //    each head (exact: bf16 x bf16 products are exact in fp32) and rho of each
-//    head split as rho_hi + rho_lo (two bf16 operands accumulated into the same
-//    fp32 result, so rho keeps ~16 significant bits). Lane l receives keys
+//    head split as rho_hi + rho_lo in two further columns (summed after the
+//    product, so rho keeps ~16 significant bits). Lane l receives keys
 //    4*(l/16) + r, r = 0..3, of column l % 16. X lives in LDS.
 //  * online softmax with a lazy rescale: the running max moves only when a
 //    score exceeds it by more than 8 (log2 units), so e <= 2^8 between
 //    rescales; the common path needs no cross-lane reduction.
-//  * weights: e for the score columns, e*p for the probe columns, moved next
-//    to each other with DPP lane moves inside 4- or 16-lane rows.
+//  * weights: e and e*p formed in the lanes of the score columns, the probe
+//    halves fetched with DPP row shifts.
 //  * weighted value sums: fp32 4x4x1 MFMA blocks with the A operand broadcast
 //    from one block (the weight rows (e_h, e_h p_h) of one key) to all 16
 //    blocks, whose B operands are 64 consecutive value dims of that key (one
@@ -62,8 +62,8 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
+constexpr int kDppRowShl4 = 0x104;   // lane i reads lane i+4 of its 16-lane row
 constexpr int kDppRowShl8 = 0x108;   // lane i reads lane i+8 of its 16-lane row
-constexpr int kDppRowShr8 = 0x118;   // lane i reads lane i-8 of its 16-lane row
 
 __device__ __forceinline__ float readlane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
@@ -71,11 +71,12 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-template <int GH>
+template <int GH, bool CORR>
 struct Layout {
   // Weight row r of MFMA set `set` -> query head of the block (-1: unused row)
-  // and whether it accumulates A (e v) or P (e p v).
-  static constexpr int NSET = GH <= 2 ? 1 : 2;
+  // and whether it accumulates A (e v) or P (e p v). Without the correction
+  // branch (plain softmax attention) only the A rows are accumulated.
+  static constexpr int NSET = (GH <= 2 || !CORR) ? 1 : 2;
   __device__ static constexpr int head(int set, int r) {
     return GH <= 2 ? (r < GH ? r : (r < 2 * GH ? r - GH : -1)) : (r < GH ? r : -1);
   }
@@ -125,9 +126,9 @@ __device__ __forceinline__ void pv_tile(const typename KV<D>::Tile& tl, const fl
   (pv_key<D, NSET, KK>(tl, w0, w1, acc), ...);
 }
 
-template <int D, int GH, bool WAVE_ITEM, int NW>
+template <int D, int GH, bool WAVE_ITEM, int NW, bool CORR>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
-  using L = Layout<GH>;
+  using L = Layout<GH, CORR>;
   using C = KV<D>;
   constexpr int NC = C::NC, TPL = C::TPL, ROW = C::ROW, NSET = L::NSET;
   constexpr int STRIDE = WAVE_ITEM ? 16 : 16 * NW;   // keys between a wave's tiles
@@ -174,45 +175,37 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   load(t0, j);
   load(t1, j + STRIDE);
 
-  // Column role of this lane in the score/probe product.
-  bool is_s, is_p;
-  int chead;
-  if constexpr (GH <= 2) {
-    is_s = qi < GH;
-    is_p = !is_s && qi < 2 * GH;
-    chead = is_s ? qi : qi - GH;
-  } else {
-    is_s = quad < 2 && qi < GH;
-    is_p = quad >= 2 && qi < GH;
-    chead = qi;
-  }
+  // Column role of this lane in the score/probe product: quad 0 holds q of
+  // head qi, quad 1 the high and quad 2 the low bf16 half of rho of head qi
+  // (quad 3 and heads >= GH are zero). The value MFMA broadcasts its weight
+  // rows from quad 0 of each 16-lane group, so only quad-0 lanes carry state.
+  const bool is_s = quad == 0 && qi < GH;
 
-  // B operands: column vector (q, or rho split hi + lo) at dims 32c + 8*grp + t,
-  // staged in LDS and re-read per tile: one copy per wave for wave items, one
-  // per workgroup (written by wave 0) for workgroup items.
+  // B operand at dims 32c + 8*grp + t, staged in LDS and re-read per tile: one
+  // copy per wave for wave items, one per workgroup (written by wave 0) for
+  // workgroup items.
   constexpr int NBS = WAVE_ITEM ? NW : 1;
   const int bslot = WAVE_ITEM ? wave : 0;
-  __shared__ u32x4 sB[NBS][2][NC][64];
+  __shared__ u32x4 sB[NBS][NC][64];
   if (WAVE_ITEM || wave == 0) {
-    const size_t bh = (size_t)b * a.Hq + h0 + chead;
+    const size_t bh = (size_t)b * a.Hq + h0 + (qi < GH ? qi : 0);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+      u32x4 v = {0u, 0u, 0u, 0u};
       const size_t off = bh * D + 32 * c + 8 * grp;
-      if (is_s) {
-        hi = *(const u32x4*)((const uint16_t*)a.q + off);
-      } else if (is_p) {
+      if (qi < GH && quad == 0) {
+        v = *(const u32x4*)((const uint16_t*)a.q + off);
+      } else if (CORR && qi < GH && (quad == 1 || quad == 2)) {
         const float4 r0 = *(const float4*)(a.rho + off);
         const float4 r1 = *(const float4*)(a.rho + off + 4);
         const float r[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          hi[w] = pack_bf16x2(r[2 * w], r[2 * w + 1]);
-          lo[w] = pack_bf16x2(r[2 * w] - bf16_lo(hi[w]), r[2 * w + 1] - bf16_hi(hi[w]));
+          const unsigned hi = pack_bf16x2(r[2 * w], r[2 * w + 1]);
+          v[w] = quad == 1 ? hi : pack_bf16x2(r[2 * w] - bf16_lo(hi), r[2 * w + 1] - bf16_hi(hi));
         }
       }
-      sB[bslot][0][c][lane] = hi;
-      sB[bslot][1][c][lane] = lo;
+      sB[bslot][c][lane] = v;
     }
   }
   if constexpr (!WAVE_ITEM) __syncthreads();
@@ -228,12 +221,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   auto compute = [&](const typename C::Tile& tl, int jt) {
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const bf16x8 bhi = as_bf16x8(sB[bslot][0][c][lane]);
-      const bf16x8 blo = as_bf16x8(sB[bslot][1][c][lane]);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[c]), bhi, sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[c]), blo, sacc, 0, 0, 0);
-    }
+    for (int c = 0; c < NC; ++c)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[c]),
+                                                     as_bf16x8(sB[bslot][c][lane]), sacc, 0, 0, 0);
     float x[4];
     float lmax = kNegInf;
 #pragma unroll
@@ -281,20 +271,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float e = is_s ? fast_exp2(x[r] - m_run) : 0.f;
+      // p = k . (rho_hi + rho_lo): the two halves sit 4 and 8 lanes up.
+      const float p = CORR ? dpp<kDppRowShl4>(sacc[r]) + dpp<kDppRowShl8>(sacc[r]) : 0.f;
+      const float ep = e * p;
       if constexpr (GH <= 2) {
-        constexpr int kQuadPerm = GH == 2 ? 0x44 : 0x00;   // lane qi reads lane qi - GH
-        const float esrc = dpp<kQuadPerm>(e);
-        w0[r] = is_s ? e : (is_p ? esrc * sacc[r] : 0.f);
+        // weight rows (e_0 .. e_{GH-1}, ep_0 .. ep_{GH-1}): lane qi >= GH takes
+        // ep of head qi - GH from its quad.
+        constexpr int kQuadPerm = GH == 2 ? 0x44 : 0x00;
+        const float eps = dpp<kQuadPerm>(ep);
+        w0[r] = qi < GH ? e : (qi < 2 * GH ? eps : 0.f);
         w1[r] = 0.f;
         lsum += w0[r];
       } else {
-        const float efrom = dpp<kDppRowShr8>(e);
-        const float ep = efrom * sacc[r];
-        const float epto = dpp<kDppRowShl8>(ep);
-        w0[r] = is_s ? e : (is_p ? efrom : 0.f);
-        w1[r] = is_s ? epto : (is_p ? ep : 0.f);
+        w0[r] = e;
+        w1[r] = ep;
         lsum += w0[r];
-        ssum += w1[r];
+        if constexpr (CORR) ssum += w1[r];
       }
     }
     pv_tile<D, NSET>(tl, w0, w1, acc, std::make_integer_sequence<int, 16>{});
@@ -361,6 +353,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     return;
   } else {
     __shared__ float sA[NW][GH][D], sP[NW][GH][D], sM[NW][GH], sL[NW][GH], sS[NW][GH];
+    if constexpr (!CORR) {   // no P rows are accumulated: the P sums are zero
+#pragma unroll
+      for (int h = 0; h < GH; ++h)
+#pragma unroll
+        for (int t = 0; t < TPL; ++t) sP[wave][h][TPL * lane + t] = 0.f;
+    }
 #pragma unroll
     for (int s = 0; s < NSET; ++s)
 #pragma unroll
@@ -414,7 +412,7 @@ int head_block(int G) {
   return 1;
 }
 
-template <int D, bool WI, int NW>
+template <int D, bool WI, int NW, bool CORR>
 hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int GH = head_block(G);
@@ -423,12 +421,19 @@ hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   if (grid > 0x7fffffffu || items > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), blk(NW * 64);
   switch (GH) {
-    case 4: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 4, WI, NW>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 3: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 3, WI, NW>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 2, WI, NW>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 1, WI, NW>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 4, WI, NW, CORR>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 3: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 3, WI, NW, CORR>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 2, WI, NW, CORR>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 1, WI, NW, CORR>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
   }
   return hipGetLastError();
+}
+
+template <bool CORR>
+hipError_t launch_d(const DecodeArgs& a, int d, int wave_items, LaunchEvents ev, hipStream_t s) {
+  if (wave_items)
+    return d == 64 ? launch_dw<64, true, 4, CORR>(a, ev, s) : launch_dw<128, true, 4, CORR>(a, ev, s);
+  return d == 64 ? launch_dw<64, false, 4, CORR>(a, ev, s) : launch_dw<128, false, 4, CORR>(a, ev, s);
 }
 
 }  // namespace
@@ -437,8 +442,8 @@ bool decode_mfma_supported(int d, int G) { return (d == 64 || d == 128) && G >= 
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, LaunchEvents ev,
                               hipStream_t s) {
-  if (wave_items) return d == 64 ? launch_dw<64, true, 4>(a, ev, s) : launch_dw<128, true, 4>(a, ev, s);
-  return d == 64 ? launch_dw<64, false, 4>(a, ev, s) : launch_dw<128, false, 4>(a, ev, s);
+  // rho == nullptr selects plain softmax attention (no correction branch).
+  return a.rho ? launch_d<true>(a, d, wave_items, ev, s) : launch_d<false>(a, d, wave_items, ev, s);
 }
 
 }  // namespace parallax

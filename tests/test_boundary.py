@@ -57,6 +57,15 @@ def test_probe_rejects_bad_arguments(L, args, code):
     assert L.parallax_last_error().decode()
 
 
+def test_softmax_decode_rejects_bad_arguments(L):
+    assert L.parallax_softmax_decode(16, 16, 16, 16, 16, 2, 3, 2, 128, 64, pb.BF16, None) == pb.ERR_INVALID_ARG
+    assert L.parallax_softmax_decode(0, 16, 16, 16, 16, 2, 4, 2, 128, 64, pb.BF16, None) == pb.ERR_INVALID_ARG
+    assert L.parallax_softmax_decode(16, 16, 16, 16, 16, 2, 4, 2, 96, 64, pb.BF16, None) == pb.ERR_UNSUPPORTED
+    # the Parallax entry point requires rho
+    assert L.parallax_decode(16, 0, 16, 16, 16, 16, 2, 4, 2, 128, 64, pb.BF16, None) == pb.ERR_INVALID_ARG
+    assert "rho" in L.parallax_last_error().decode()
+
+
 def test_options_and_profile_on_host(L):
     assert L.parallax_set_option(pb.OPT_CHUNK, 100) == pb.ERR_INVALID_ARG
     assert L.parallax_set_option(pb.OPT_ITEMS, 3) == pb.ERR_INVALID_ARG

@@ -202,6 +202,35 @@ def test_bitwise_repeatable_and_output_guards():
     assert torch.all(buf[:guard] == 12345.0) and torch.all(buf[guard + n:] == 12345.0)
 
 
+@pytest.mark.parametrize("Hq,Hkv,dtype,kernel,items", [(16, 8, "bf16", 0, 0), (32, 8, "bf16", 0, 0),
+                                                      (16, 8, "bf16", 0, 2), (32, 8, "bf16", 2, 1),
+                                                      (12, 4, "bf16", 0, 0), (4, 2, "f32", 0, 0)])
+def test_softmax_only_variant(Hq, Hkv, dtype, kernel, items):
+    """parallax_softmax_decode: plain softmax attention over the same cache (the
+    W_R = 0 reduction) against the oracle with rho = 0 and torch SDPA (fp64)."""
+    wl = WORKLOADS[2].scaled(B=4, Hq=Hq, Hkv=Hkv, ctx=3000, d_model=64, dtype=dtype)
+    s = make_inputs(wl, 8, lengths=[3000, 1, 0, 1777])
+    say(f"[case] softmax-only Hq={Hq} Hkv={Hkv} {dtype} kernel={kernel} items={items}")
+    dev = Device(s)
+    with pb.options(kernel=kernel, items=items):
+        o = to64(pb.softmax_decode(dev.q, dev.K, dev.V, dev.seq_lens, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    ref = oracle_out(s, np.zeros((wl.B, wl.Hq, wl.d)))
+    G = Hq // Hkv
+    for b, n in enumerate(s.seq_lens.tolist()):
+        if n == 0:
+            continue
+        qt = s.q[b].double()[:, None, :]
+        kt = s.K[b].double().repeat_interleave(G, dim=0)
+        vt = s.V[b].double().repeat_interleave(G, dim=0)
+        sdpa = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, 0].numpy()
+        np.testing.assert_allclose(ref[b], sdpa, rtol=0, atol=1e-12)
+    tol = 1e-5 if dtype == "f32" else 2e-6
+    say(f"softmax-only: rel {rel_l2(o, ref):.3e} max_abs {max_abs(o, ref):.3e}")
+    assert rel_l2(o, ref) <= tol and max_abs(o, ref) <= 1e-4
+    assert np.all(o[2] == 0.0)
+
+
 def test_workspace_grows_across_shapes_and_streams():
     """The per-stream split-K workspace grows when a larger shape arrives and
     its arrival counters return to zero after every call (smaller shapes after
