@@ -232,8 +232,9 @@ def run_workload(args, wl_id: int, emit: bool = True):
 
 
 def run_sweep(args):
-    """Batch x context sweep at Hq=16, Hkv=8, d=128 bf16 (decode only, rotated
-    K/V so that every rep reads cold data); one JSON line per point."""
+    """Batch x context sweep at Hq=16, Hkv=8, d=128 bf16 (decode split-K pass +
+    merge, rotated K/V sets so that every rep reads cold data); one JSON line
+    per point. GB/s counts K/V, q, rho, out and seq_lens."""
     import torch
     from parallax_covariance_corrected_amd import binding as pb
     from parallax_covariance_corrected_amd.workloads import sweep_points
@@ -246,8 +247,8 @@ def run_sweep(args):
         g = torch.Generator(device=dev).manual_seed(B * 100003 + ctx)
         sets = []
         for _ in range(nsets):
-            K = torch.randn((B, 8, ctx, 128), generator=g, device=dev).to(torch.bfloat16)
-            V = torch.randn((B, 8, ctx, 128), generator=g, device=dev).to(torch.bfloat16)
+            K = torch.randn((B, 8, ctx, 128), generator=g, device=dev, dtype=torch.bfloat16)
+            V = torch.randn((B, 8, ctx, 128), generator=g, device=dev, dtype=torch.bfloat16)
             sets.append((K, V))
         q = torch.randn((B, 16, 128), generator=g, device=dev).to(torch.bfloat16)
         rho = torch.randn((B, 16, 128), generator=g, device=dev) * 0.1
@@ -267,7 +268,9 @@ def run_sweep(args):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         byts = kv + B * 16 * 128 * (2 + 4 + 2) + B * 4
-        print(json.dumps({"sweep": True, "B": B, "ctx": ctx, "us_per_step": round(us, 2),
+        chunk, splits, kern = pb.decode_plan(B, 16, 8, 128, ctx)
+        print(json.dumps({"sweep": True, "B": B, "ctx": ctx, "plan": [chunk, splits, kern],
+                          "us_per_step": round(us, 2),
                           "tokens_per_s": round(B / (us * 1e-6), 1),
                           "gbps": round(byts / (us * 1e-6) / 1e9, 1),
                           "pct_peak": round(100 * byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)}),
