@@ -8,10 +8,10 @@
 // or LDS staging of operands is needed. Products of bf16 values are exact in
 // fp32 and the accumulation is fp32.
 //
-// bf16 kernel: a workgroup of NW waves owns a (16*MT rows) x (16*NT columns)
-// tile; its waves split K NW ways, each issuing the loads of U k-steps before
-// their MFMAs, and reduce through LDS in a fixed order. Rows past B read zeros
-// (buffer range).
+// bf16, small batch (B <= 64): a workgroup of NW waves owns a (16*MT rows) x
+// 16 columns tile; its waves split K NW ways, each issuing the loads of U
+// k-steps before their MFMAs, and reduce through LDS in a fixed order. Rows
+// past B read zeros (buffer range). Larger batches use an LDS-tiled GEMM.
 // fp32 kernel: one thread per output, a plain dot product.
 #include "common.h"
 
@@ -95,6 +95,114 @@ __global__ __launch_bounds__(NW * 64) void probe_mfma_kernel(const uint16_t* __r
   }
 }
 
+// Large-batch probe: a 128 x 128 tile of rho per workgroup, eight waves in a
+// 4 x 2 arrangement each owning 32 x 64 (2 x 4 MFMA tiles). K advances in
+// steps of 64 through double-buffered LDS, so every workgroup reads its x and
+// W_R panels from the caches once. LDS rows are 128 bytes (eight 16-byte
+// chunks); chunk c of row r sits at slot c ^ ((r >> 1) & 7). With that swizzle
+// the 16 rows one MFMA operand read touches, and the two rows a quarter-wave
+// stores, fall in distinct bank groups (no conflicts, no padding).
+constexpr int kGM = 128, kGN = 128, kGK = 64;
+constexpr int kGWM = 4, kGWN = 2;                  // wave grid
+constexpr int kGTI = kGM / 16 / kGWM;              // MFMA tiles per wave, rows
+constexpr int kGTJ = kGN / 16 / kGWN;              // MFMA tiles per wave, columns
+constexpr int kGThreads = 64 * kGWM * kGWN;
+constexpr int kRowChunks = kGK / 8;                // 16-byte chunks per LDS row
+constexpr int kLdsRow = kGK * 2;
+constexpr int kLoadsA = kGM * kRowChunks / kGThreads, kLoadsB = kGN * kRowChunks / kGThreads;
+
+__device__ __forceinline__ int lds_slot(int row, int chunk) {
+  return row * kLdsRow + 16 * (chunk ^ ((row >> 1) & (kRowChunks - 1)));
+}
+
+__global__ __launch_bounds__(kGThreads) void probe_gemm_kernel(const uint16_t* __restrict__ W,
+                                                               const uint16_t* __restrict__ x,
+                                                               float* __restrict__ rho, int B,
+                                                               int N, int K) {
+  __shared__ __attribute__((aligned(16))) unsigned char sA[2][kGM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) unsigned char sB[2][kGN * kLdsRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int wm = wave / kGWN, wn = wave % kGWN;
+  const int m0 = blockIdx.y * kGM, n0 = blockIdx.x * kGN;
+  const unsigned rowb = (unsigned)K * 2;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (size_t)m0 * K, (unsigned)min(B - m0, kGM) * rowb);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + (size_t)n0 * K, (unsigned)min(N - n0, kGN) * rowb);
+
+  // Global -> registers -> LDS: load c of thread t moves chunk (t + c*threads)
+  // of the tile, row-major (consecutive threads read consecutive 16 bytes).
+  u32x4 ga[kLoadsA], gb[kLoadsB];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < kLoadsA; ++c) {
+      const int idx = tid + c * kGThreads, kk = k0 + 8 * (idx % kRowChunks);
+      ga[c] = buf_load16(xr, kk < K ? (unsigned)(idx / kRowChunks) * rowb + (unsigned)kk * 2 : 0x80000000u);
+    }
+#pragma unroll
+    for (int c = 0; c < kLoadsB; ++c) {
+      const int idx = tid + c * kGThreads, kk = k0 + 8 * (idx % kRowChunks);
+      gb[c] = buf_load16(wr, kk < K ? (unsigned)(idx / kRowChunks) * rowb + (unsigned)kk * 2 : 0x80000000u);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < kLoadsA; ++c) {
+      const int idx = tid + c * kGThreads;
+      *(u32x4*)&sA[buf][lds_slot(idx / kRowChunks, idx % kRowChunks)] = ga[c];
+    }
+#pragma unroll
+    for (int c = 0; c < kLoadsB; ++c) {
+      const int idx = tid + c * kGThreads;
+      *(u32x4*)&sB[buf][lds_slot(idx / kRowChunks, idx % kRowChunks)] = gb[c];
+    }
+  };
+
+  f32x4 acc[kGTI][kGTJ];
+#pragma unroll
+  for (int i = 0; i < kGTI; ++i)
+#pragma unroll
+    for (int jn = 0; jn < kGTJ; ++jn) acc[i][jn] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (K + kGK - 1) / kGK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * kGK);   // next panels in flight
+#pragma unroll
+    for (int ks = 0; ks < kGK / 32; ++ks) {
+      u32x4 av[kGTI], bv[kGTJ];
+#pragma unroll
+      for (int i = 0; i < kGTI; ++i)
+        av[i] = *(const u32x4*)&sA[cur][lds_slot(wm * 16 * kGTI + 16 * i + l16, 4 * ks + grp)];
+#pragma unroll
+      for (int jn = 0; jn < kGTJ; ++jn)
+        bv[jn] = *(const u32x4*)&sB[cur][lds_slot(wn * 16 * kGTJ + 16 * jn + l16, 4 * ks + grp)];
+#pragma unroll
+      for (int i = 0; i < kGTI; ++i)
+#pragma unroll
+        for (int jn = 0; jn < kGTJ; ++jn)
+          acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(bv[jn]),
+                                                                acc[i][jn], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);   // the other buffer was last read before the barrier
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < kGTI; ++i)
+#pragma unroll
+    for (int jn = 0; jn < kGTJ; ++jn) {
+      const int col = n0 + wn * 16 * kGTJ + 16 * jn + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * 16 * kGTI + 16 * i + 4 * grp + r;
+        if (row < B && col < N) rho[(size_t)row * N + col] = acc[i][jn][r];
+      }
+    }
+}
+
 __global__ __launch_bounds__(256) void probe_f32_kernel(const float* __restrict__ W,
                                                         const float* __restrict__ x,
                                                         float* __restrict__ rho, int B, int N,
@@ -124,8 +232,8 @@ hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, 
   const uint16_t* Wb = (const uint16_t*)W;
   const uint16_t* xb = (const uint16_t*)x;
   if (B > 64) {
-    dim3 grid((N + 63) / 64, (B + 63) / 64);
-    hipExtLaunchKernelGGL((probe_mfma_kernel<4, 4, 4, 2>), grid, dim3(256), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
+    dim3 grid((N + kGN - 1) / kGN, (B + kGM - 1) / kGM);
+    hipExtLaunchKernelGGL(probe_gemm_kernel, grid, dim3(kGThreads), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
   } else {
     const int mt = (B + 15) / 16;
     dim3 grid((N + 15) / 16, 1);

@@ -253,12 +253,14 @@ def test_workspace_grows_across_shapes_and_streams():
                 assert rel_l2(to64(o), ref) <= 1e-5
 
 
-@pytest.mark.parametrize("B,d_model,dtype", [(1, 2048, "bf16"), (17, 2560, "bf16"), (64, 2048, "bf16"),
-                                             (65, 512, "bf16"), (130, 72, "bf16"), (3, 100, "f32")])
-def test_probe_shapes(B, d_model, dtype):
-    wl = WORKLOADS[2].scaled(B=B, d_model=d_model, ctx=16, dtype=dtype)
+@pytest.mark.parametrize("B,d_model,dtype,Hq,d", [
+    (1, 2048, "bf16", 16, 128), (17, 2560, "bf16", 16, 128), (64, 2048, "bf16", 16, 128),
+    (65, 512, "bf16", 16, 128), (130, 72, "bf16", 16, 128), (3, 100, "f32", 16, 128),
+    (2048, 2048, "bf16", 16, 128), (300, 520, "bf16", 3, 64), (129, 4096, "bf16", 5, 128)])
+def test_probe_shapes(B, d_model, dtype, Hq, d):
+    wl = WORKLOADS[2].scaled(B=B, d_model=d_model, ctx=16, dtype=dtype, Hq=Hq, Hkv=1, d=d)
     s = make_inputs(wl, 7)
-    say(f"[case] probe B={B} d_model={d_model} {dtype}")
+    say(f"[case] probe B={B} d_model={d_model} Hq={Hq} d={d} {dtype}")
     rho = pb.probe(s.W_R.cuda(), s.x.cuda(), wl.Hq, wl.d)
     torch.cuda.synchronize()
     e = rel_l2(to64(rho), oracle_rho(s))
