@@ -3,7 +3,8 @@ imported by tests, the smoke check and the bench's CPU-baseline leg, never by
 the product path). ``oracle.lla_oracle`` adds the exact local-linear-attention
 reference (a per-query conjugate-gradient solve) that Parallax replaces."""
 from .parallax_oracle import (probe, softmax_weights, weighted_means, kv_covariance,
-                              decode_head, decode, decode_heads, kv_head_of)
+                              decode_head, decode, decode_heads, kv_head_of, prefill,
+                              prefill_rows)
 
 __all__ = ["probe", "softmax_weights", "weighted_means", "kv_covariance",
-           "decode_head", "decode", "decode_heads", "kv_head_of"]
+           "decode_head", "decode", "decode_heads", "kv_head_of", "prefill", "prefill_rows"]

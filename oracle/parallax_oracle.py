@@ -35,7 +35,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["probe", "softmax_weights", "weighted_means", "kv_covariance",
-           "decode_head", "decode", "decode_heads", "kv_head_of"]
+           "decode_head", "decode", "decode_heads", "kv_head_of", "prefill", "prefill_rows"]
 
 
 def _f64(a) -> np.ndarray:
@@ -144,4 +144,46 @@ def decode_heads(q, rho, K_parts, V_parts, seq_lens, Hkv: int, pairs) -> np.ndar
         g = kv_head_of(h, Hq, Hkv)
         Kb, Vb = _seq_kv(K_parts, V_parts, b, g, n)
         res.append(decode_head(q[b, h], rho[b, h], Kb, Vb))
+    return np.stack(res)
+
+
+def prefill(q, rho, K_parts, V_parts, prefix_lens, Hkv: int) -> np.ndarray:
+    """Causal many-query forward (prefill) -> [B, T, Hq, d].
+
+    Token t of sequence b sits at position prefix_lens[b] + t of its cache and
+    attends to cache rows 0 .. prefix_lens[b] + t (itself and everything
+    before it); each (token, head) output is the Parallax output of that query
+    over that prefix: decode_head with the token's own query and probe. The
+    layer is pretrained as the attention of a language model at a 4096-token
+    context (encorp.ai (de), section "Die Pretraining-Gewinne sind real ...");
+    the causal prefix is the reading taken for that forward pass (the pages do
+    not spell the mask out), and decode is its one-token case.
+    q, rho: [B, T, Hq, d]; K_parts/V_parts: per-sequence [Hkv, n_b, d] arrays
+    holding at least prefix_lens[b] + T rows (or a padded cache).
+    """
+    qa = _f64(q)
+    ra = _f64(rho)
+    B, T, Hq, d = qa.shape
+    pre = [int(p) for p in _f64(prefix_lens)]
+    out = np.zeros((B, T, Hq, d))
+    for b in range(B):
+        for t in range(T):
+            n = pre[b] + t + 1
+            for h in range(Hq):
+                g = kv_head_of(h, Hq, Hkv)
+                Kb, Vb = _seq_kv(K_parts, V_parts, b, g, n)
+                out[b, t, h] = decode_head(qa[b, t, h], ra[b, t, h], Kb, Vb)
+    return out
+
+
+def prefill_rows(q, rho, K_parts, V_parts, prefix_lens, Hkv: int, rows) -> np.ndarray:
+    """prefill() restricted to the listed (b, t, h) rows -> [len(rows), d]."""
+    qa = _f64(q)
+    ra = _f64(rho)
+    Hq = qa.shape[2]
+    res = []
+    for b, t, h in rows:
+        n = int(prefix_lens[b]) + t + 1
+        Kb, Vb = _seq_kv(K_parts, V_parts, b, kv_head_of(h, Hq, Hkv), n)
+        res.append(decode_head(qa[b, t, h], ra[b, t, h], Kb, Vb))
     return np.stack(res)
