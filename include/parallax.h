@@ -122,6 +122,35 @@ int parallax_softmax_decode(const void* q, const void* k_cache, const void* v_ca
                             const int* seq_lens, void* out, int B, int Hq, int Hkv, int d,
                             int max_ctx, int dtype, hipStream_t stream);
 
+/*
+ * parallax_prefill — the causal many-query forward (prefill or chunked
+ * prefill): T new tokens per sequence, each attending to the cache up to and
+ * including its own position. The layer is pretrained as language-model
+ * attention (encorp.ai (de), section "Die Pretraining-Gewinne sind real ...");
+ * the causal prefix is the reading taken, and each token's output is the
+ * Parallax output of parallax_decode over its prefix with its own query and
+ * probe (zubnet.ai (pt), second paragraph).
+ *
+ * Token t (0 <= t < T) of sequence b sits at cache position P_b + t, with
+ * P_b = prefix_lens[b] (0 when prefix_lens is null), and attends to cache rows
+ * 0 .. P_b + t of KV head g = h / (Hq / Hkv). The caller has written the K/V
+ * rows of the new tokens into the cache at P_b .. P_b + T - 1.
+ *
+ *   q           : [B, T, Hq, d]            bf16
+ *   rho         : [B, T, Hq, d]            fp32 (from parallax_probe on the B*T tokens)
+ *   k_cache     : [B, Hkv, max_ctx, d]     bf16; rows >= P_b + T are never read
+ *   v_cache     : [B, Hkv, max_ctx, d]     same layout as k_cache
+ *   prefix_lens : [B] int32, device memory, or null; 0 <= P_b <= max_ctx - T
+ *   out         : [B, T, Hq, d]            bf16 (PARALLAX_BF16) or fp32 (PARALLAX_BF16_F32OUT)
+ *
+ * Requires 1 <= T <= max_ctx and the decode shape rules; PARALLAX_F32 is
+ * UNSUPPORTED here. P_b outside 0 .. max_ctx - T is clamped on the device
+ * (memory safety; a caller error). No workspace; enqueue-only on `stream`.
+ */
+int parallax_prefill(const void* q, const float* rho, const void* k_cache, const void* v_cache,
+                     const int* prefix_lens, void* out, int B, int T, int Hq, int Hkv, int d,
+                     int max_ctx, int dtype, hipStream_t stream);
+
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char* parallax_last_error(void);
 
@@ -160,7 +189,7 @@ int parallax_get_option(int option, int* value);
  * Kernel timing when PARALLAX_OPT_PROFILE is 1: every launch carries start and
  * stop HIP events stamped by its own dispatch (hipExtLaunchKernel), so the
  * timing adds no work between kernels. kernel: 0 = probe, 1 = decode
- * (split-K pass), 2 = merge.
+ * (split-K pass), 2 = merge, 3 = prefill.
  * parallax_profile_read waits for the recorded events and returns the summed
  * duration (ms) and the number of launches since the last reset.
  */

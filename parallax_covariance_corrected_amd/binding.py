@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_MEMORY = 0, 1, 2, 3, 4
 F32, BF16, BF16_F32OUT = 0, 1, 2
 OPT_CHUNK, OPT_KERNEL, OPT_PROFILE, OPT_ITEMS = 1, 2, 3, 4
-KERNEL_PROBE, KERNEL_DECODE, KERNEL_MERGE = 0, 1, 2
+KERNEL_PROBE, KERNEL_DECODE, KERNEL_MERGE, KERNEL_PREFILL = 0, 1, 2, 3
 
 _lib = None
 
@@ -43,6 +43,7 @@ def lib() -> ctypes.CDLL:
         L.parallax_probe.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
         L.parallax_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
         L.parallax_softmax_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
         L.parallax_decode_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i),
                                            ctypes.POINTER(i), ctypes.POINTER(i)]
         L.parallax_set_option.argtypes = [i, i]
@@ -51,7 +52,7 @@ def lib() -> ctypes.CDLL:
                                             ctypes.POINTER(ctypes.c_longlong)]
         L.parallax_profile_reset.argtypes = []
         for name in ("parallax_probe", "parallax_decode", "parallax_softmax_decode",
-                     "parallax_decode_plan",
+                     "parallax_prefill", "parallax_decode_plan",
                      "parallax_set_option", "parallax_get_option", "parallax_profile_read",
                      "parallax_profile_reset"):
             getattr(L, name).restype = i
@@ -155,6 +156,35 @@ def softmax_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     code = _dtype_code(q.dtype, out.dtype)
     _check(lib().parallax_softmax_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
                                          _ptr(out), B, Hq, Hkv, d, max_ctx, code, _stream()))
+    return out
+
+
+def prefill(q: torch.Tensor, rho: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+            prefix_lens: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """Causal many-query forward: out[B, T, Hq, d] for q [B, T, Hq, d] (bf16),
+    rho [B, T, Hq, d] (fp32) and a cache [B, Hkv, max_ctx, d] holding each
+    sequence's prefix_lens[b] cached tokens followed by its T new ones."""
+    for t, nm in ((q, "q"), (rho, "rho"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm)
+    B, T, Hq, d = q.shape
+    _, Hkv, max_ctx, _ = k_cache.shape
+    if rho.dtype != torch.float32 or tuple(rho.shape) != (B, T, Hq, d):
+        raise ValueError("rho must be float32 [B, T, Hq, d]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, k_cache and v_cache must share a dtype")
+    pp = None
+    if prefix_lens is not None:
+        _need(prefix_lens, "prefix_lens")
+        if prefix_lens.dtype != torch.int32:
+            raise ValueError("prefix_lens must be int32")
+        pp = _ptr(prefix_lens)
+    if out is None:
+        out = torch.empty((B, T, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out")
+    code = _dtype_code(q.dtype, out.dtype)
+    _check(lib().parallax_prefill(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), pp, _ptr(out),
+                                  B, T, Hq, Hkv, d, max_ctx, code, _stream()))
     return out
 
 

@@ -43,7 +43,7 @@ struct Timing {
   long long launches = 0;
 };
 std::mutex g_prof_mu;
-Timing g_prof[3];
+Timing g_prof[4];   // probe, decode, merge, prefill
 std::vector<hipEvent_t> g_event_pool;
 
 hipEvent_t take_event() {
@@ -248,7 +248,7 @@ int parallax_profile_reset(void) {
 }
 
 int parallax_profile_read(int kernel, double* total_ms, long long* launches) {
-  if (kernel < 0 || kernel > 2) return fail(PARALLAX_ERR_INVALID_ARG, "kernel must be 0, 1 or 2");
+  if (kernel < 0 || kernel > 3) return fail(PARALLAX_ERR_INVALID_ARG, "kernel must be 0, 1, 2 or 3");
   if (!total_ms || !launches) return fail(PARALLAX_ERR_INVALID_ARG, "null output pointer");
   std::lock_guard<std::mutex> g(g_prof_mu);
   Timing& t = g_prof[kernel];
@@ -380,6 +380,47 @@ int parallax_softmax_decode(const void* q, const void* k_cache, const void* v_ca
                             int max_ctx, int dtype, hipStream_t stream) {
   return decode_impl(q, nullptr, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, d, max_ctx, dtype,
                      stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int parallax_prefill(const void* q, const float* rho, const void* k_cache, const void* v_cache,
+                     const int* prefix_lens, void* out, int B, int T, int Hq, int Hkv, int d,
+                     int max_ctx, int dtype, hipStream_t stream) {
+  if (dtype == PARALLAX_F32)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "prefill takes bf16 inputs (dtype BF16 or BF16_F32OUT)");
+  int rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
+  if (rc != PARALLAX_OK) return rc;
+  if (T < 1 || T > max_ctx) return fail(PARALLAX_ERR_INVALID_ARG, "T must be in 1 .. max_ctx");
+  if (!q || !rho || !k_cache || !v_cache || !out)
+    return fail(PARALLAX_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(q, 16) || !aligned(rho, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, 16) || (prefix_lens && !aligned(prefix_lens, 4)))
+    return fail(PARALLAX_ERR_INVALID_ARG, "pointers must be 16-byte aligned (prefix_lens 4-byte)");
+  if (B > 65535 || Hkv > 65535 || (long long)T * (Hq / Hkv) > (1LL << 30) ||
+      (long long)B * T * Hq > (1LL << 40))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "prefill size out of range");
+  parallax::PrefillArgs a;
+  a.q = q;
+  a.rho = rho;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.prefix = prefix_lens;
+  a.out = out;
+  a.B = B;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.max_ctx = max_ctx;
+  a.out_f32 = dtype == PARALLAX_BF16 ? 0 : 1;
+  a.scale_log2 = parallax::kLog2e / sqrtf((float)d);
+  const parallax::LaunchEvents ev = profile_events();
+  hipError_t e = parallax::launch_prefill_mfma(a, d, ev, stream);
+  profile_record(3, ev, e == hipSuccess);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return PARALLAX_OK;
 }
 
 }  // extern "C"

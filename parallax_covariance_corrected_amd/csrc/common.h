@@ -91,6 +91,20 @@ struct DecodeArgs {
   float scale_log2;  // log2(e) / sqrt(d)
 };
 
+// Causal many-query forward: token t of sequence b is at cache position
+// prefix[b] + t and attends to cache rows 0 .. prefix[b] + t.
+struct PrefillArgs {
+  const void* q;        // [B, T, Hq, d] bf16
+  const float* rho;     // [B, T, Hq, d] fp32
+  const void* k;        // [B, Hkv, max_ctx, d] bf16
+  const void* v;
+  const int* prefix;    // [B] device, or null (all 0)
+  void* out;            // [B, T, Hq, d] bf16 or fp32
+  int B, T, Hq, Hkv, max_ctx;
+  int out_f32;
+  float scale_log2;
+};
+
 __device__ __forceinline__ void store_output(const DecodeArgs& a, size_t idx, float o) {
   if (a.out_f32) store_out<float>((float*)a.out + idx, o);
   else store_out<uint16_t>((uint16_t*)a.out + idx, o);
@@ -112,6 +126,7 @@ hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, Lau
 hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, LaunchEvents ev,
                               hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, int d, LaunchEvents ev, hipStream_t s);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int d, LaunchEvents ev, hipStream_t s);
 bool decode_mfma_supported(int d, int G);
 hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, int K,
                         int f32_inputs, LaunchEvents ev, hipStream_t s);

@@ -1,0 +1,286 @@
+// Causal many-query Parallax forward (prefill) on the bf16 matrix cores.
+//
+// Token t of sequence b sits at cache position prefix[b] + t and attends to
+// cache rows 0 .. prefix[b] + t; its output is softmax attention minus the
+// softmax-weighted KV covariance times its own probe (zubnet.ai (pt),
+// "Parallax mantém softmax ...", second paragraph), in the one-pass form
+//   out = A/l - (P/l - (A/l)(S/l)),  l = sum e, S = sum e p, A = sum e v,
+//   P = sum e p v,  e = exp(s - m),  s = q.k/sqrt(d),  p = k.rho.
+//
+// Work: a workgroup owns 64 rows of one (sequence, KV head): rows are the
+// flattened (token, query head of the group) pairs, so the G query heads that
+// share a KV head share every K/V tile. Four waves of 16 rows. Keys advance in
+// blocks of 64 through double-buffered LDS (K row-major, V transposed to
+// dim-major), up to the last key any row of the workgroup may see; a wave skips
+// the blocks that lie entirely after its own rows.
+//
+// Everything is computed transposed (keys x rows), which keeps every step in
+// the lane that produced it:
+//  * S^T = K Q^T and Pr^T = K R^T with bf16 16x16x32 MFMAs (K tile as the A
+//    operand from LDS, q and rho of the wave's rows as B operands in
+//    registers). q.k products of bf16 are exact in fp32; rho enters as two bf16
+//    terms hi + lo accumulated into the same product (16 significant bits).
+//    Lane l receives keys 4*(l/16) + r of row l % 16.
+//  * online softmax per row (lane's row = l % 16) with a lazy rescale: the
+//    running max moves only when a block max exceeds it by more than 8 (log2
+//    units).
+//  * weights e and e*p in fp32, split into bf16 hi + lo (a bf16 weight alone
+//    would cost ~1e-3 relative error), become the B operand of O^T = V^T E^T
+//    directly from the registers that hold them: the MFMA's k slots are bound
+//    to keys (4*(l/16) + t of two 16-key sub-tiles), and the A operand V^T
+//    reads the same keys from the transposed V tile.
+#include "common.h"
+
+namespace parallax {
+namespace {
+
+constexpr int kPfRows = 64;        // rows per workgroup
+constexpr int kPfKeys = 64;        // keys per block
+constexpr int kPfThreads = 256;
+constexpr float kPfRescale = 8.0f;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+// K tile: row = key, D*2 bytes; 16-byte chunk c of row r at slot c ^ f(r),
+// with f chosen so that the 16 rows one operand read touches fall in distinct
+// bank groups.
+template <int D>
+__device__ __forceinline__ int k_slot(int row, int chunk) {
+  if constexpr (D == 128) return row * 256 + 16 * (chunk ^ (row & 15));
+  else return row * 128 + 16 * (chunk ^ ((row >> 1) & 7));
+}
+// V^T tile: row = dim, 64 keys * 2 bytes + 8 bytes of padding.
+constexpr int kVtRow = kPfKeys * 2 + 8;
+
+template <int D>
+struct PfSmem {
+  unsigned char k[2][kPfKeys * D * 2];
+  unsigned char vt[2][D * kVtRow];
+};
+
+__device__ __forceinline__ unsigned pk2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+
+template <int D, bool F32_OUT>
+__global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int NKS = D / 32;            // 32-dim k-steps of the score product
+  constexpr int NDT = D / 16;            // 16-dim output tiles
+  constexpr int ROW = D * 2;             // bytes per K/V cache row
+  constexpr int CPR = D / 8;             // 16-byte chunks per cache row
+  constexpr int LOADS = kPfKeys * CPR / kPfThreads;   // 16-byte loads per thread per block
+  __shared__ __attribute__((aligned(16))) PfSmem<D> sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int G = a.Hq / a.Hkv;
+  const int TG = a.T * G;
+  const int nrb = (TG + kPfRows - 1) / kPfRows;
+  const int rb = nrb - 1 - (int)blockIdx.x;          // heaviest row blocks first
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int F0 = rb * kPfRows;
+  int prefix = a.prefix ? a.prefix[b] : 0;
+  prefix = min(max(prefix, 0), a.max_ctx - a.T);
+  const int nvalid = prefix + a.T;                   // cache rows that exist
+
+  // Rows of this lane (column of the transposed products) and of the wave.
+  const int F = F0 + 16 * wave + l16;
+  const bool row_ok = F < TG;
+  const int tok = row_ok ? F / G : 0;
+  const int head = g * G + (row_ok ? F % G : 0);
+  const int pos = row_ok ? prefix + tok : -1;        // last key this row sees
+  const int Fw_last = min(F0 + 16 * wave + 15, TG - 1);
+  const int wave_last_key = F0 + 16 * wave < TG ? prefix + Fw_last / G : -1;
+  const int wg_last_key = prefix + (min(F0 + kPfRows, TG) - 1) / G;
+  const int nkb = wg_last_key / kPfKeys + 1;
+
+  // K/V of (b, g): rows past nvalid read as zero (buffer range).
+  const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)a.max_ctx * D;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc((const uint16_t*)a.k + kv_base, (unsigned)nvalid * ROW);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const uint16_t*)a.v + kv_base, (unsigned)nvalid * ROW);
+
+  // Loads of one key block: K chunk-fastest (a row per 16 or 8 lanes, rows
+  // contiguous), V key-fastest (a wave covers 64 keys of one 8-dim chunk, so
+  // the transposed stores of a wave fill one V^T row).
+  u32x4 kreg[LOADS], vreg[LOADS];
+  auto gload = [&](int kb) {
+    const unsigned base = (unsigned)kb * kPfKeys * ROW;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int idx = threadIdx.x + i * kPfThreads;
+      kreg[i] = buf_load16(krs, base + (unsigned)(idx / CPR) * ROW + 16u * (idx % CPR));
+      vreg[i] = buf_load16(vrs, base + (unsigned)(idx % kPfKeys) * ROW + 16u * (idx / kPfKeys));
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int idx = threadIdx.x + i * kPfThreads;
+      *(u32x4*)&sm.k[buf][k_slot<D>(idx / CPR, idx % CPR)] = kreg[i];
+      const int key = idx % kPfKeys, c = idx / kPfKeys;
+      unsigned char* vt = &sm.vt[buf][(8 * c) * kVtRow + 2 * key];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const unsigned w = vreg[i][e >> 1];
+        *(uint16_t*)(vt + e * kVtRow) = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+      }
+    }
+  };
+
+  gload(0);   // start streaming before the q/rho prologue
+
+  // q and rho of this lane's row as B operands: dims 32*ks + 8*grp .. +7.
+  u32x4 qb[NKS], rh[NKS], rl[NKS];
+  {
+    const size_t off = (((size_t)b * a.T + tok) * a.Hq + head) * D + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 qv = {0u, 0u, 0u, 0u}, hv = {0u, 0u, 0u, 0u}, lv = {0u, 0u, 0u, 0u};
+      if (row_ok) {
+        qv = *(const u32x4*)((const uint16_t*)a.q + off + 32 * ks);
+        const float4 r0 = *(const float4*)(a.rho + off + 32 * ks);
+        const float4 r1 = *(const float4*)(a.rho + off + 32 * ks + 4);
+        const float r[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const unsigned hi = pk2(r[2 * w], r[2 * w + 1]);
+          hv[w] = hi;
+          lv[w] = pk2(r[2 * w] - bf16_lo(hi), r[2 * w + 1] - bf16_hi(hi));
+        }
+      }
+      qb[ks] = qv;
+      rh[ks] = hv;
+      rl[ks] = lv;
+    }
+  }
+
+  f32x4 oa[NDT], op[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) {
+    oa[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    op[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+  float m_run = kNegInf, lpart = 0.f, spart = 0.f;
+
+  lstore(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < nkb) gload(kb + 1);
+    if (kb * kPfKeys <= wave_last_key) {
+      // ---- scores and probes, 4 sub-tiles of 16 keys
+      f32x4 s[4], pr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        pr[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8 kv = as_bf16x8(*(const u32x4*)&sm.k[cur][k_slot<D>(16 * j + l16, 4 * ks + grp)]);
+          s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(qb[ks]), s[j], 0, 0, 0);
+          pr[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(rh[ks]), pr[j], 0, 0, 0);
+          pr[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(rl[ks]), pr[j], 0, 0, 0);
+        }
+      }
+      // ---- scale, causal mask, block max of this lane's row
+      float bmax = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb * kPfKeys + 16 * j + 4 * grp + r;
+          const float x = key <= pos ? s[j][r] * a.scale_log2 : kNegInf;
+          s[j][r] = x;
+          bmax = fmaxf(bmax, x);
+        }
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      if (bmax > m_run + kPfRescale) {   // lazy: move the max only by a margin
+        const float c = rescale(m_run, bmax);
+        m_run = bmax;
+        lpart *= c;
+        spart *= c;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) {
+          oa[i] *= c;
+          op[i] *= c;
+        }
+      }
+      // ---- weights, then O^T += V^T (e, e*p)^T per 32-key step
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        float e[8], ep[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int j = 2 * h2 + (t >> 2), r = t & 3;
+          const float x = s[j][r];
+          e[t] = x == kNegInf ? 0.f : fast_exp2(x - m_run);
+          ep[t] = e[t] * pr[j][r];
+          lpart += e[t];
+          spart += ep[t];
+        }
+        u32x4 eh, el, ph, pl;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          eh[w] = pk2(e[2 * w], e[2 * w + 1]);
+          el[w] = pk2(e[2 * w] - bf16_lo(eh[w]), e[2 * w + 1] - bf16_hi(eh[w]));
+          ph[w] = pk2(ep[2 * w], ep[2 * w + 1]);
+          pl[w] = pk2(ep[2 * w] - bf16_lo(ph[w]), ep[2 * w + 1] - bf16_hi(ph[w]));
+        }
+        // A operand: V^T rows 16*dt + l16, keys 32*h2 + 4*grp .. +3 and
+        // 32*h2 + 16 + 4*grp .. +3 (the keys bound to k slots t = 0..7).
+        const unsigned char* vrow = &sm.vt[cur][l16 * kVtRow + 2 * (32 * h2 + 4 * grp)];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const u32x2 v0 = *(const u32x2*)(vrow + dt * 16 * kVtRow);
+          const u32x2 v1 = *(const u32x2*)(vrow + dt * 16 * kVtRow + 32);
+          const bf16x8 va = as_bf16x8((u32x4){v0[0], v0[1], v1[0], v1[1]});
+          oa[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(eh), oa[dt], 0, 0, 0);
+          oa[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(el), oa[dt], 0, 0, 0);
+          op[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(ph), op[dt], 0, 0, 0);
+          op[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(pl), op[dt], 0, 0, 0);
+        }
+      }
+    }
+    if (kb + 1 < nkb) lstore(cur ^ 1);   // that stage was last read before the barrier
+    __syncthreads();
+  }
+
+  // ---- epilogue: row sums over the 4 lanes of the row, then out
+  lpart += __shfl_xor(lpart, 16);
+  lpart += __shfl_xor(lpart, 32);
+  spart += __shfl_xor(spart, 16);
+  spart += __shfl_xor(spart, 32);
+  if (!row_ok) return;
+  const size_t obase = (((size_t)b * a.T + tok) * a.Hq + head) * D + 4 * grp;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    float o[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = parallax_out(oa[dt][r], op[dt][r], lpart, spart);
+    if constexpr (F32_OUT) {
+      *(float4*)((float*)a.out + obase + 16 * dt) = make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+      *(u32x2*)((uint16_t*)a.out + obase + 16 * dt) = (u32x2){pk2(o[0], o[1]), pk2(o[2], o[3])};
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int d, LaunchEvents ev, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  const long long rows = (long long)a.T * G;
+  const long long nrb = (rows + kPfRows - 1) / kPfRows;
+  if (nrb > 0x7fffffffLL || a.Hkv > 65535 || a.B > 65535) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)nrb, (unsigned)a.Hkv, (unsigned)a.B);
+  if (d == 128) {
+    if (a.out_f32) hipExtLaunchKernelGGL((prefill_mfma_kernel<128, true>), grid, dim3(kPfThreads), 0, s, ev.start, ev.stop, 0, a);
+    else hipExtLaunchKernelGGL((prefill_mfma_kernel<128, false>), grid, dim3(kPfThreads), 0, s, ev.start, ev.stop, 0, a);
+  } else {
+    if (a.out_f32) hipExtLaunchKernelGGL((prefill_mfma_kernel<64, true>), grid, dim3(kPfThreads), 0, s, ev.start, ev.stop, 0, a);
+    else hipExtLaunchKernelGGL((prefill_mfma_kernel<64, false>), grid, dim3(kPfThreads), 0, s, ev.start, ev.stop, 0, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace parallax

@@ -152,6 +152,44 @@ def make_inputs(wl: Workload, seed: int = 0, *, wr_zero: bool = False,
     return InputSet(wl, seed, x, W_R, q, seq, K, V)
 
 
+@dataclass
+class PrefillSet:
+    """Inputs of a causal many-query forward: T new tokens per sequence after
+    prefix[b] cached ones (K/V hold prefix[b] + T rows per sequence)."""
+    wl: Workload
+    seed: int
+    T: int
+    prefix: torch.Tensor          # [B] int32
+    x: torch.Tensor               # [B, T, d_model]
+    W_R: torch.Tensor             # [Hq*d, d_model]
+    q: torch.Tensor               # [B, T, Hq, d]
+    K: List[torch.Tensor]         # per sequence [Hkv, prefix[b] + T, d]
+    V: List[torch.Tensor]
+
+    @property
+    def max_ctx(self) -> int:
+        return int(self.prefix.max()) + self.T
+
+
+def make_prefill_inputs(wl: Workload, T: int, prefix: List[int], seed: int = 0) -> PrefillSet:
+    """Draw a prefill input set: x [B, T, d_model], W_R, q [B, T, Hq, d], then
+    per sequence K and V of prefix[b] + T rows, with the distributions of
+    make_inputs (bf16 rounding of scaled fp32 normals)."""
+    if len(prefix) != wl.B or min(prefix) < 0:
+        raise ValueError("prefix must have B non-negative entries")
+    dt = torch_dtype(wl.dtype)
+    g = torch.Generator("cpu").manual_seed(seed)
+    x = _normal(g, (wl.B, T, wl.d_model), 1.0, dt)
+    W_R = _normal(g, (wl.Hq * wl.d, wl.d_model), wl.wr_std, dt)
+    q = _normal(g, (wl.B, T, wl.Hq, wl.d), 1.0, dt)
+    K, V = [], []
+    for b in range(wl.B):
+        n = prefix[b] + T
+        K.append(_normal(g, (wl.Hkv, n, wl.d), wl.k_scale, dt))
+        V.append(_normal(g, (wl.Hkv, n, wl.d), 1.0, dt))
+    return PrefillSet(wl, seed, T, torch.tensor(prefix, dtype=torch.int32), x, W_R, q, K, V)
+
+
 def padded_cache(parts: List[torch.Tensor], max_ctx: int, pad: float = float("nan"),
                  device="cpu") -> torch.Tensor:
     """Lay per-sequence [Hkv, n_b, d] tensors into a [B, Hkv, max_ctx, d] cache.

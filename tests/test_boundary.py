@@ -57,6 +57,28 @@ def test_probe_rejects_bad_arguments(L, args, code):
     assert L.parallax_last_error().decode()
 
 
+def _prefill(L, *, q=16, rho=16, k=16, v=16, pre=16, out=16, B=2, T=8, Hq=4, Hkv=2, d=128,
+             max_ctx=64, dtype=pb.BF16):
+    return L.parallax_prefill(q, rho, k, v, pre, out, B, T, Hq, Hkv, d, max_ctx, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dtype=pb.F32), pb.ERR_UNSUPPORTED, "bf16"),
+    (dict(T=0), pb.ERR_INVALID_ARG, "T must"),
+    (dict(T=65), pb.ERR_INVALID_ARG, "T must"),
+    (dict(Hq=3, Hkv=2), pb.ERR_INVALID_ARG, "multiple"),
+    (dict(d=32), pb.ERR_UNSUPPORTED, "64 or 128"),
+    (dict(rho=0), pb.ERR_INVALID_ARG, "null"),
+    (dict(out=0), pb.ERR_INVALID_ARG, "null"),
+    (dict(q=24), pb.ERR_INVALID_ARG, "aligned"),
+    (dict(pre=18), pb.ERR_INVALID_ARG, "aligned"),
+    (dict(B=70000), pb.ERR_UNSUPPORTED, "range"),
+])
+def test_prefill_rejects_bad_arguments(L, kw, code, msg):
+    assert _prefill(L, **kw) == code
+    assert msg in L.parallax_last_error().decode()
+
+
 def test_softmax_decode_rejects_bad_arguments(L):
     assert L.parallax_softmax_decode(16, 16, 16, 16, 16, 2, 3, 2, 128, 64, pb.BF16, None) == pb.ERR_INVALID_ARG
     assert L.parallax_softmax_decode(0, 16, 16, 16, 16, 2, 4, 2, 128, 64, pb.BF16, None) == pb.ERR_INVALID_ARG
