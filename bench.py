@@ -279,6 +279,60 @@ def run_sweep(args):
         torch.cuda.empty_cache()
 
 
+def run_prefill(args):
+    """Causal many-query forward (parallax_prefill) on the mid-context heads
+    (Hq=16, Hkv=8, d=128, bf16) at B sequences of T new tokens, no prefix.
+    Algorithmic work: 8d flops per visible (query head, key) pair (q.k, k.rho,
+    e v and e p v), Hq * B * T (T + 1) / 2 pairs; bound by the bf16 matrix
+    cores (2.5 PFLOP/s dense)."""
+    import torch
+    from parallax_covariance_corrected_amd import binding as pb
+    B, T, Hq, Hkv, d = args.prefill_B, args.prefill_T, 16, 8, 128
+    g = torch.Generator(device="cuda").manual_seed(0)
+    q = torch.randn((B, T, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    rho = torch.randn((B, T, Hq, d), generator=g, device="cuda") * 0.9
+    K = torch.randn((B, Hkv, T, d), generator=g, device="cuda").to(torch.bfloat16)
+    V = torch.randn((B, Hkv, T, d), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
+    print(f"# bench: prefill B={B} T={T} Hq={Hq} Hkv={Hkv} d={d}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        pb.prefill(q, rho, K, V, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        pb.prefill(q, rho, K, V, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    with pb.options(profile=1):
+        pb.profile_reset()
+        for _ in range(args.steps):
+            pb.prefill(q, rho, K, V, out=out)
+        torch.cuda.synchronize()
+        tot, n = pb.profile_read(pb.KERNEL_PREFILL)
+    kern_us = tot * 1000.0 / max(n, 1)
+    pairs = Hq * B * T * (T + 1) // 2
+    flops = 8 * d * pairs
+    achieved = flops / (kern_us * 1e-6) / 1e12
+    line = {
+        "metric": "Parallax prefill tokens/s (causal, many-query forward)",
+        "value": round(B * T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill_B{B}_T{T}_Hq{Hq}_Hkv{Hkv}_d{d}", "B": B, "T": T, "Hq": Hq,
+                   "Hkv": Hkv, "d": d, "prefix": 0},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(achieved / 2500.0, 4), "traffic": None,
+                     "kernel": "prefill_mfma_kernel", "algorithmic_flops_per_launch": flops,
+                     "avg_launch_us": round(kern_us, 3),
+                     "mfma_flops_issued_per_launch_note":
+                         "14d per (row, key) incl. bf16 hi/lo splits, whole 64-key blocks"},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +346,10 @@ def main():
                     help="first copy 256 MiB device-to-device 3 times (a kernel of known "
                          "traffic, to scale hardware byte counters)")
     ap.add_argument("--sweep-max-gib", type=int, default=0)
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure the causal many-query forward instead of decode")
+    ap.add_argument("--prefill-T", type=int, default=4096)
+    ap.add_argument("--prefill-B", type=int, default=1)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the Parallax decode path here is built and "
@@ -312,6 +370,9 @@ def main():
         del src, dst
     if args.sweep:
         run_sweep(args)
+        return
+    if args.prefill:
+        run_prefill(args)
         return
     run_workload(args, args.workload)
 

@@ -28,9 +28,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
-// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even.
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even, in
+// one v_cvt_pk_bf16_f32.
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  return (unsigned)f32_to_bf16_rne(lo) | ((unsigned)f32_to_bf16_rne(hi) << 16);
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Raw buffer resource over [base, base + bytes): loads at byte offsets past

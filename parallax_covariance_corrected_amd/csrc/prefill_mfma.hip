@@ -90,6 +90,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
   const int pos = row_ok ? prefix + tok : -1;        // last key this row sees
   const int Fw_last = min(F0 + 16 * wave + 15, TG - 1);
   const int wave_last_key = F0 + 16 * wave < TG ? prefix + Fw_last / G : -1;
+  // Smallest position of the wave's rows (-1 when it holds rows past the end):
+  // key blocks that end at or before it need no causal mask.
+  const int wave_first_key = Fw_last == F0 + 16 * wave + 15 ? prefix + (F0 + 16 * wave) / G : -1;
   const int wg_last_key = prefix + (min(F0 + kPfRows, TG) - 1) / G;
   const int nkb = wg_last_key / kPfKeys + 1;
 
@@ -167,36 +170,61 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
     const int cur = kb & 1;
     if (kb + 1 < nkb) gload(kb + 1);
     if (kb * kPfKeys <= wave_last_key) {
-      // ---- scores and probes, 4 sub-tiles of 16 keys
+      // ---- scores and probes, 4 sub-tiles of 16 keys. k-steps outside,
+      // sub-tiles inside: eight independent accumulators between dependent
+      // MFMAs; the K operands of the next k-step are read ahead.
       f32x4 s[4], pr[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         s[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
         pr[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+      u32x4 kcur[4], knext[4];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 kv = as_bf16x8(*(const u32x4*)&sm.k[cur][k_slot<D>(16 * j + l16, 4 * ks + grp)]);
-          s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(qb[ks]), s[j], 0, 0, 0);
-          pr[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(rh[ks]), pr[j], 0, 0, 0);
-          pr[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(rl[ks]), pr[j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) kcur[j] = *(const u32x4*)&sm.k[cur][k_slot<D>(16 * j + l16, grp)];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 1 < NKS) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            knext[j] = *(const u32x4*)&sm.k[cur][k_slot<D>(16 * j + l16, 4 * (ks + 1) + grp)];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[j]), as_bf16x8(qb[ks]), s[j], 0, 0, 0);
+          pr[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[j]), as_bf16x8(rh[ks]), pr[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pr[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[j]), as_bf16x8(rl[ks]), pr[j], 0, 0, 0);
+        if (ks + 1 < NKS) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) kcur[j] = knext[j];
         }
       }
-      // ---- scale, causal mask, block max of this lane's row
+      // ---- causal mask (only blocks that reach past a row of the wave), block
+      // max of this lane's row on the raw scores
+      if (kb * kPfKeys + kPfKeys - 1 > wave_first_key) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kb * kPfKeys + 16 * j + 4 * grp + r > pos) s[j][r] = kNegInf;
+      }
       float bmax = kNegInf;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kb * kPfKeys + 16 * j + 4 * grp + r;
-          const float x = key <= pos ? s[j][r] * a.scale_log2 : kNegInf;
-          s[j][r] = x;
-          bmax = fmaxf(bmax, x);
-        }
+        for (int r = 0; r < 4; ++r) bmax = fmaxf(bmax, s[j][r]);
       bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      if (bmax > m_run + kPfRescale) {   // lazy: move the max only by a margin
-        const float c = rescale(m_run, bmax);
-        m_run = bmax;
+      bmax *= a.scale_log2;   // log2 domain
+      // Lazy rescale: the running max moves only when the block max exceeds it
+      // by a margin; the branch is taken by the whole wave, rarely.
+      const bool moves = bmax > m_run + kPfRescale;
+      if (__any(moves)) {
+        const float c = moves ? rescale(m_run, bmax) : 1.f;
+        m_run = moves ? bmax : m_run;
         lpart *= c;
         spart *= c;
 #pragma unroll
@@ -205,6 +233,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
           op[i] *= c;
         }
       }
+      // A row with no key yet keeps m = -inf; its scores are all -inf, and
+      // exp2(-inf - 0) = 0.
+      const float neg_m = m_run == kNegInf ? 0.f : -m_run;
       // ---- weights, then O^T += V^T (e, e*p)^T per 32-key step
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -212,8 +243,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int j = 2 * h2 + (t >> 2), r = t & 3;
-          const float x = s[j][r];
-          e[t] = x == kNegInf ? 0.f : fast_exp2(x - m_run);
+          e[t] = fast_exp2(fmaf(s[j][r], a.scale_log2, neg_m));
           ep[t] = e[t] * pr[j][r];
           lpart += e[t];
           spart += ep[t];
@@ -229,16 +259,29 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
         // A operand: V^T rows 16*dt + l16, keys 32*h2 + 4*grp .. +3 and
         // 32*h2 + 16 + 4*grp .. +3 (the keys bound to k slots t = 0..7).
         const unsigned char* vrow = &sm.vt[cur][l16 * kVtRow + 2 * (32 * h2 + 4 * grp)];
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
+        auto vload = [&](int dt) {
           const u32x2 v0 = *(const u32x2*)(vrow + dt * 16 * kVtRow);
           const u32x2 v1 = *(const u32x2*)(vrow + dt * 16 * kVtRow + 32);
-          const bf16x8 va = as_bf16x8((u32x4){v0[0], v0[1], v1[0], v1[1]});
-          oa[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(eh), oa[dt], 0, 0, 0);
-          oa[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(el), oa[dt], 0, 0, 0);
-          op[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(ph), op[dt], 0, 0, 0);
-          op[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(pl), op[dt], 0, 0, 0);
+          return (u32x4){v0[0], v0[1], v1[0], v1[1]};
+        };
+        // hi terms of tile dt, then lo terms of tile dt - 1: no accumulator is
+        // hit by two MFMAs in a row.
+        u32x4 vprev = vload(0);
+        u32x4 vcur = vprev;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const u32x4 vnext = dt + 1 < NDT ? vload(dt + 1) : vcur;
+          oa[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vcur), as_bf16x8(eh), oa[dt], 0, 0, 0);
+          op[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vcur), as_bf16x8(ph), op[dt], 0, 0, 0);
+          if (dt > 0) {
+            oa[dt - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vprev), as_bf16x8(el), oa[dt - 1], 0, 0, 0);
+            op[dt - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vprev), as_bf16x8(pl), op[dt - 1], 0, 0, 0);
+          }
+          vprev = vcur;
+          vcur = vnext;
         }
+        oa[NDT - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vprev), as_bf16x8(el), oa[NDT - 1], 0, 0, 0);
+        op[NDT - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vprev), as_bf16x8(pl), op[NDT - 1], 0, 0, 0);
       }
     }
     if (kb + 1 < nkb) lstore(cur ^ 1);   // that stage was last read before the barrier
