@@ -30,11 +30,16 @@ sys.path.insert(0, ROOT)
 METRIC = "Parallax decode tokens/s and HBM GB/s (% of peak) over batch×context sweep"
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak, GB/s
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SRC = os.path.join(ROOT, "parallax_covariance_corrected_amd", "csrc", "decode_mfma.hip")
+# The decode kernel's source: its own file and the shared device header.
+DECODE_SRCS = [os.path.join(ROOT, "parallax_covariance_corrected_amd", "csrc", f)
+               for f in ("decode_mfma.hip", "common.h")]
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in DECODE_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload_name: str):
