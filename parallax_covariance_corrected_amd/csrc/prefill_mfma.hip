@@ -60,6 +60,23 @@ struct PfSmem {
 
 __device__ __forceinline__ unsigned pk2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
+// A row's four lanes are l16 + 16*grp, grp = 0..3. The permlane swaps (gfx950)
+// hand every lane the value of the lane 16 apart and then 32 apart, in
+// registers (no LDS round trip): after a swap each lane holds its own value
+// and its partner's.
+__device__ __forceinline__ float row_max4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D, bool F32_OUT>
 __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NKS = D / 32;            // 32-dim k-steps of the score product
@@ -216,9 +233,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) bmax = fmaxf(bmax, s[j][r]);
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      bmax *= a.scale_log2;   // log2 domain
+      bmax = row_max4(bmax) * a.scale_log2;   // log2 domain
       // Lazy rescale: the running max moves only when the block max exceeds it
       // by a margin; the branch is taken by the whole wave, rarely.
       const bool moves = bmax > m_run + kPfRescale;
@@ -289,10 +304,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
   }
 
   // ---- epilogue: row sums over the 4 lanes of the row, then out
-  lpart += __shfl_xor(lpart, 16);
-  lpart += __shfl_xor(lpart, 32);
-  spart += __shfl_xor(spart, 16);
-  spart += __shfl_xor(spart, 32);
+  lpart = row_sum4(lpart);
+  spart = row_sum4(spart);
   if (!row_ok) return;
   const size_t obase = (((size_t)b * a.T + tok) * a.Hq + head) * D + 4 * grp;
 #pragma unroll
