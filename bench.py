@@ -320,6 +320,26 @@ def run_prefill(args):
     pairs = Hq * B * T * (T + 1) // 2
     flops = 8 * d * pairs
     achieved = flops / (kern_us * 1e-6) / 1e12
+
+    # Matched ratios: the softmax-only forward on the same inputs (same bytes,
+    # half the algorithmic flops) and with twice the query heads (same flops).
+    def kernel_us(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        with pb.options(profile=1):
+            pb.profile_reset()
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            t, c = pb.profile_read(pb.KERNEL_PREFILL)
+        return t * 1000.0 / max(c, 1)
+    soft_us = kernel_us(lambda: pb.prefill(q, None, K, V, out=out))
+    q2 = torch.randn((B, T, 2 * Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    out2 = torch.empty((B, T, 2 * Hq, d), dtype=torch.bfloat16, device="cuda")
+    soft2_us = kernel_us(lambda: pb.prefill(q2, None, K, V, out=out2))
+    del q2, out2
+    cpu = prefill_cpu_baseline(q, rho, K, V, budget_s=args.cpu_budget) if args.cpu_baseline else None
     line = {
         "metric": "Parallax prefill tokens/s (causal, many-query forward)",
         "value": round(B * T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -334,8 +354,41 @@ def run_prefill(args):
                      "avg_launch_us": round(kern_us, 3),
                      "mfma_flops_issued_per_launch_note":
                          "14d per (row, key) incl. bf16 hi/lo splits, whole 64-key blocks"},
+        "cpu_baseline": cpu,
+        "matched": {"parallax_prefill_us": round(kern_us, 3), "softmax_prefill_us": round(soft_us, 3),
+                    "softmax_2x_heads_prefill_us": round(soft2_us, 3),
+                    "io_matched_speedup": round(soft_us / kern_us, 4),
+                    "compute_matched_speedup": round(soft2_us / kern_us, 4)},
     }
     print(json.dumps(line), flush=True)
+
+
+def prefill_cpu_baseline(q, rho, K, V, budget_s: float = 12.0):
+    """The fp64 oracle on a bounded sample of (token, head) rows, scaled to the
+    whole forward. Tokens are drawn uniformly, so the mean cost per row is an
+    unbiased estimate (a row's cost grows with its token index)."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    B, T, Hq, d = q.shape
+    qh = q.float().cpu().numpy().astype(np.float64)
+    rh = rho.cpu().numpy().astype(np.float64)
+    Kp = [K[b].float().cpu().numpy().astype(np.float64) for b in range(B)]
+    Vp = [V[b].float().cpu().numpy().astype(np.float64) for b in range(B)]
+    Hkv = K.shape[1]
+    pre = np.zeros(B, dtype=np.int64)
+    r = np.random.default_rng(0)
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        rows = [(int(r.integers(0, B)), int(r.integers(0, T)), int(r.integers(0, Hq))) for _ in range(8)]
+        oracle.prefill_rows(qh, rh, Kp, Vp, pre, Hkv, rows)
+        done += len(rows)
+    el = time.perf_counter() - t0
+    full_s = el / done * (B * T * Hq)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(B * T / full_s, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle on {done} uniformly drawn (token, head) rows of {B * T * Hq} "
+                      f"in {el:.1f} s, scaled to the whole forward"}
 
 
 def main():
@@ -355,6 +408,7 @@ def main():
                     help="measure the causal many-query forward instead of decode")
     ap.add_argument("--prefill-T", type=int, default=4096)
     ap.add_argument("--prefill-B", type=int, default=1)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the Parallax decode path here is built and "

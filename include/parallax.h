@@ -151,6 +151,17 @@ int parallax_prefill(const void* q, const float* rho, const void* k_cache, const
                      const int* prefix_lens, void* out, int B, int T, int Hq, int Hkv, int d,
                      int max_ctx, int dtype, hipStream_t stream);
 
+/*
+ * parallax_softmax_prefill — the same causal forward without the correction
+ * branch (plain softmax attention, the W_R = 0 reduction; encorp.ai (de),
+ * section "Parallax behält Softmax bei"): the baseline that prices the
+ * correction in the compute-bound regime. Arguments, layouts and errors as
+ * parallax_prefill, without rho.
+ */
+int parallax_softmax_prefill(const void* q, const void* k_cache, const void* v_cache,
+                             const int* prefix_lens, void* out, int B, int T, int Hq, int Hkv,
+                             int d, int max_ctx, int dtype, hipStream_t stream);
+
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char* parallax_last_error(void);
 

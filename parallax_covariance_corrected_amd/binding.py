@@ -44,6 +44,7 @@ def lib() -> ctypes.CDLL:
         L.parallax_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
         L.parallax_softmax_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
         L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+        L.parallax_softmax_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
         L.parallax_decode_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i),
                                            ctypes.POINTER(i), ctypes.POINTER(i)]
         L.parallax_set_option.argtypes = [i, i]
@@ -52,7 +53,7 @@ def lib() -> ctypes.CDLL:
                                             ctypes.POINTER(ctypes.c_longlong)]
         L.parallax_profile_reset.argtypes = []
         for name in ("parallax_probe", "parallax_decode", "parallax_softmax_decode",
-                     "parallax_prefill", "parallax_decode_plan",
+                     "parallax_prefill", "parallax_softmax_prefill", "parallax_decode_plan",
                      "parallax_set_option", "parallax_get_option", "parallax_profile_read",
                      "parallax_profile_reset"):
             getattr(L, name).restype = i
@@ -159,18 +160,22 @@ def softmax_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     return out
 
 
-def prefill(q: torch.Tensor, rho: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-            prefix_lens: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+def prefill(q: torch.Tensor, rho: Optional[torch.Tensor], k_cache: torch.Tensor,
+            v_cache: torch.Tensor, prefix_lens: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None,
             out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     """Causal many-query forward: out[B, T, Hq, d] for q [B, T, Hq, d] (bf16),
     rho [B, T, Hq, d] (fp32) and a cache [B, Hkv, max_ctx, d] holding each
-    sequence's prefix_lens[b] cached tokens followed by its T new ones."""
-    for t, nm in ((q, "q"), (rho, "rho"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+    sequence's prefix_lens[b] cached tokens followed by its T new ones.
+    rho=None runs plain softmax attention (parallax_softmax_prefill)."""
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _need(t, nm)
     B, T, Hq, d = q.shape
     _, Hkv, max_ctx, _ = k_cache.shape
-    if rho.dtype != torch.float32 or tuple(rho.shape) != (B, T, Hq, d):
-        raise ValueError("rho must be float32 [B, T, Hq, d]")
+    if rho is not None:
+        _need(rho, "rho")
+        if rho.dtype != torch.float32 or tuple(rho.shape) != (B, T, Hq, d):
+            raise ValueError("rho must be float32 [B, T, Hq, d]")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q, k_cache and v_cache must share a dtype")
     pp = None
@@ -183,8 +188,12 @@ def prefill(q: torch.Tensor, rho: torch.Tensor, k_cache: torch.Tensor, v_cache: 
         out = torch.empty((B, T, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
     _need(out, "out")
     code = _dtype_code(q.dtype, out.dtype)
-    _check(lib().parallax_prefill(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), pp, _ptr(out),
-                                  B, T, Hq, Hkv, d, max_ctx, code, _stream()))
+    if rho is None:
+        _check(lib().parallax_softmax_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), pp, _ptr(out),
+                                              B, T, Hq, Hkv, d, max_ctx, code, _stream()))
+    else:
+        _check(lib().parallax_prefill(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), pp,
+                                      _ptr(out), B, T, Hq, Hkv, d, max_ctx, code, _stream()))
     return out
 
 

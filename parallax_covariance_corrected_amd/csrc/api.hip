@@ -384,19 +384,20 @@ int parallax_softmax_decode(const void* q, const void* k_cache, const void* v_ca
 
 }  // extern "C"
 
-extern "C" {
+namespace {
 
-int parallax_prefill(const void* q, const float* rho, const void* k_cache, const void* v_cache,
-                     const int* prefix_lens, void* out, int B, int T, int Hq, int Hkv, int d,
-                     int max_ctx, int dtype, hipStream_t stream) {
+// Shared by parallax_prefill and parallax_softmax_prefill (rho == nullptr).
+int prefill_impl(const void* q, const float* rho, const void* k_cache, const void* v_cache,
+                 const int* prefix_lens, void* out, int B, int T, int Hq, int Hkv, int d,
+                 int max_ctx, int dtype, hipStream_t stream) {
   if (dtype == PARALLAX_F32)
     return fail(PARALLAX_ERR_UNSUPPORTED, "prefill takes bf16 inputs (dtype BF16 or BF16_F32OUT)");
   int rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
   if (rc != PARALLAX_OK) return rc;
   if (T < 1 || T > max_ctx) return fail(PARALLAX_ERR_INVALID_ARG, "T must be in 1 .. max_ctx");
-  if (!q || !rho || !k_cache || !v_cache || !out)
+  if (!q || !k_cache || !v_cache || !out)
     return fail(PARALLAX_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned(q, 16) || !aligned(rho, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+  if (!aligned(q, 16) || (rho && !aligned(rho, 16)) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(out, 16) || (prefix_lens && !aligned(prefix_lens, 4)))
     return fail(PARALLAX_ERR_INVALID_ARG, "pointers must be 16-byte aligned (prefix_lens 4-byte)");
   if (B > 65535 || Hkv > 65535 || (long long)T * (Hq / Hkv) > (1LL << 30) ||
@@ -421,6 +422,25 @@ int parallax_prefill(const void* q, const float* rho, const void* k_cache, const
   profile_record(3, ev, e == hipSuccess);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return PARALLAX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int parallax_prefill(const void* q, const float* rho, const void* k_cache, const void* v_cache,
+                     const int* prefix_lens, void* out, int B, int T, int Hq, int Hkv, int d,
+                     int max_ctx, int dtype, hipStream_t stream) {
+  if (!rho) return fail(PARALLAX_ERR_INVALID_ARG, "null pointer argument (rho)");
+  return prefill_impl(q, rho, k_cache, v_cache, prefix_lens, out, B, T, Hq, Hkv, d, max_ctx,
+                      dtype, stream);
+}
+
+int parallax_softmax_prefill(const void* q, const void* k_cache, const void* v_cache,
+                             const int* prefix_lens, void* out, int B, int T, int Hq, int Hkv,
+                             int d, int max_ctx, int dtype, hipStream_t stream) {
+  return prefill_impl(q, nullptr, k_cache, v_cache, prefix_lens, out, B, T, Hq, Hkv, d, max_ctx,
+                      dtype, stream);
 }
 
 }  // extern "C"

@@ -77,7 +77,8 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, bool F32_OUT>
+// CORR = false: plain softmax attention (no probe products, no e*p sums).
+template <int D, bool F32_OUT, bool CORR>
 __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NKS = D / 32;            // 32-dim k-steps of the score product
   constexpr int NDT = D / 16;            // 16-dim output tiles
@@ -157,6 +158,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
       u32x4 qv = {0u, 0u, 0u, 0u}, hv = {0u, 0u, 0u, 0u}, lv = {0u, 0u, 0u, 0u};
       if (row_ok) {
         qv = *(const u32x4*)((const uint16_t*)a.q + off + 32 * ks);
+      }
+      if (CORR && row_ok) {
         const float4 r0 = *(const float4*)(a.rho + off + 32 * ks);
         const float4 r1 = *(const float4*)(a.rho + off + 32 * ks + 4);
         const float r[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
@@ -209,11 +212,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[j]), as_bf16x8(qb[ks]), s[j], 0, 0, 0);
-          pr[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[j]), as_bf16x8(rh[ks]), pr[j], 0, 0, 0);
+          if constexpr (CORR)
+            pr[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[j]), as_bf16x8(rh[ks]), pr[j], 0, 0, 0);
         }
+        if constexpr (CORR) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          pr[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[j]), as_bf16x8(rl[ks]), pr[j], 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            pr[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[j]), as_bf16x8(rl[ks]), pr[j], 0, 0, 0);
+        }
         if (ks + 1 < NKS) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) kcur[j] = knext[j];
@@ -259,17 +265,19 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
         for (int t = 0; t < 8; ++t) {
           const int j = 2 * h2 + (t >> 2), r = t & 3;
           e[t] = fast_exp2(fmaf(s[j][r], a.scale_log2, neg_m));
-          ep[t] = e[t] * pr[j][r];
+          ep[t] = CORR ? e[t] * pr[j][r] : 0.f;
           lpart += e[t];
-          spart += ep[t];
+          if constexpr (CORR) spart += ep[t];
         }
         u32x4 eh, el, ph, pl;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           eh[w] = pk2(e[2 * w], e[2 * w + 1]);
           el[w] = pk2(e[2 * w] - bf16_lo(eh[w]), e[2 * w + 1] - bf16_hi(eh[w]));
-          ph[w] = pk2(ep[2 * w], ep[2 * w + 1]);
-          pl[w] = pk2(ep[2 * w] - bf16_lo(ph[w]), ep[2 * w + 1] - bf16_hi(ph[w]));
+          if constexpr (CORR) {
+            ph[w] = pk2(ep[2 * w], ep[2 * w + 1]);
+            pl[w] = pk2(ep[2 * w] - bf16_lo(ph[w]), ep[2 * w + 1] - bf16_hi(ph[w]));
+          }
         }
         // A operand: V^T rows 16*dt + l16, keys 32*h2 + 4*grp .. +3 and
         // 32*h2 + 16 + 4*grp .. +3 (the keys bound to k slots t = 0..7).
@@ -287,16 +295,19 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
         for (int dt = 0; dt < NDT; ++dt) {
           const u32x4 vnext = dt + 1 < NDT ? vload(dt + 1) : vcur;
           oa[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vcur), as_bf16x8(eh), oa[dt], 0, 0, 0);
-          op[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vcur), as_bf16x8(ph), op[dt], 0, 0, 0);
+          if constexpr (CORR)
+            op[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vcur), as_bf16x8(ph), op[dt], 0, 0, 0);
           if (dt > 0) {
             oa[dt - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vprev), as_bf16x8(el), oa[dt - 1], 0, 0, 0);
-            op[dt - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vprev), as_bf16x8(pl), op[dt - 1], 0, 0, 0);
+            if constexpr (CORR)
+              op[dt - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vprev), as_bf16x8(pl), op[dt - 1], 0, 0, 0);
           }
           vprev = vcur;
           vcur = vnext;
         }
         oa[NDT - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vprev), as_bf16x8(el), oa[NDT - 1], 0, 0, 0);
-        op[NDT - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vprev), as_bf16x8(pl), op[NDT - 1], 0, 0, 0);
+        if constexpr (CORR)
+          op[NDT - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vprev), as_bf16x8(pl), op[NDT - 1], 0, 0, 0);
       }
     }
     if (kb + 1 < nkb) lstore(cur ^ 1);   // that stage was last read before the barrier
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
 
   // ---- epilogue: row sums over the 4 lanes of the row, then out
   lpart = row_sum4(lpart);
-  spart = row_sum4(spart);
+  if constexpr (CORR) spart = row_sum4(spart);
   if (!row_ok) return;
   const size_t obase = (((size_t)b * a.T + tok) * a.Hq + head) * D + 4 * grp;
 #pragma unroll
@@ -323,18 +334,27 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
 
 }  // namespace
 
+template <int D, bool CORR>
+void launch_pf(const PrefillArgs& a, dim3 grid, LaunchEvents ev, hipStream_t s) {
+  if (a.out_f32)
+    hipExtLaunchKernelGGL((prefill_mfma_kernel<D, true, CORR>), grid, dim3(kPfThreads), 0, s, ev.start, ev.stop, 0, a);
+  else
+    hipExtLaunchKernelGGL((prefill_mfma_kernel<D, false, CORR>), grid, dim3(kPfThreads), 0, s, ev.start, ev.stop, 0, a);
+}
+
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int d, LaunchEvents ev, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const long long rows = (long long)a.T * G;
   const long long nrb = (rows + kPfRows - 1) / kPfRows;
   if (nrb > 0x7fffffffLL || a.Hkv > 65535 || a.B > 65535) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)nrb, (unsigned)a.Hkv, (unsigned)a.B);
+  // rho == nullptr selects plain softmax attention (no correction branch).
   if (d == 128) {
-    if (a.out_f32) hipExtLaunchKernelGGL((prefill_mfma_kernel<128, true>), grid, dim3(kPfThreads), 0, s, ev.start, ev.stop, 0, a);
-    else hipExtLaunchKernelGGL((prefill_mfma_kernel<128, false>), grid, dim3(kPfThreads), 0, s, ev.start, ev.stop, 0, a);
+    if (a.rho) launch_pf<128, true>(a, grid, ev, s);
+    else launch_pf<128, false>(a, grid, ev, s);
   } else {
-    if (a.out_f32) hipExtLaunchKernelGGL((prefill_mfma_kernel<64, true>), grid, dim3(kPfThreads), 0, s, ev.start, ev.stop, 0, a);
-    else hipExtLaunchKernelGGL((prefill_mfma_kernel<64, false>), grid, dim3(kPfThreads), 0, s, ev.start, ev.stop, 0, a);
+    if (a.rho) launch_pf<64, true>(a, grid, ev, s);
+    else launch_pf<64, false>(a, grid, ev, s);
   }
   return hipGetLastError();
 }

@@ -77,6 +77,25 @@ def test_prefill_matches_oracle(Hq, Hkv, d, T, prefix):
     np.testing.assert_array_equal(obf, bf16_rne(o32))
 
 
+@pytest.mark.parametrize("Hq,Hkv,d,T,prefix", [(4, 2, 128, 150, [0, 70]), (8, 2, 64, 65, [3, 0])])
+def test_softmax_prefill_matches_oracle(Hq, Hkv, d, T, prefix):
+    """rho = None: plain causal softmax attention (the oracle with rho = 0)."""
+    wl = WORKLOADS[2].scaled(B=len(prefix), Hq=Hq, Hkv=Hkv, d=d, d_model=256)
+    s = make_prefill_inputs(wl, T, prefix, seed=3 * T)
+    say(f"[case] softmax prefill Hq={Hq} Hkv={Hkv} d={d} T={T} prefix={prefix}")
+    K = padded_cache(s.K, s.max_ctx, device="cuda")
+    V = padded_cache(s.V, s.max_ctx, device="cuda")
+    o32 = to64(pb.prefill(s.q.cuda(), None, K, V, s.prefix.cuda(), out_dtype=torch.float32))
+    obf = to64(pb.prefill(s.q.cuda(), None, K, V, s.prefix.cuda()))
+    torch.cuda.synchronize()
+    ref = oracle.prefill(s.q, np.zeros((len(prefix), T, Hq, d)), s.K, s.V, s.prefix.numpy(), Hkv)
+    e = rel_l2(o32, ref)
+    say(f"softmax prefill: f32 rel {e:.2e}, bf16 rel {rel_l2(obf, ref):.2e}")
+    assert e <= F32OUT_REL and max_abs(o32, ref) <= F32OUT_ABS
+    assert rel_l2(obf, ref) <= BF16_REL_L2
+    np.testing.assert_array_equal(obf, bf16_rne(o32))
+
+
 def test_prefill_without_prefix_pointer_and_larger_cache():
     """prefix_lens = null means no cached prefix; a cache larger than needed
     (NaN beyond the valid rows) changes nothing."""
