@@ -10,8 +10,10 @@
 // included) were finished by the decode kernel and are skipped.
 //
 // One workgroup per (sequence, query head): its 4 waves take interleaved
-// splits (loads of several splits in flight per wave), lanes own D/64 dims,
-// and the waves' sums are combined through LDS in a fixed order.
+// splits, lanes own D/64 dims. Each wave folds its splits with a running max
+// (so the state and partial-sum loads of all its splits are issued together:
+// one memory round trip), then the four wave states are combined through LDS
+// in a fixed order.
 #include "common.h"
 
 namespace parallax {
@@ -20,6 +22,7 @@ namespace {
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   constexpr int DPL = D / 64;   // dims per lane
+  constexpr int U = 4;          // splits per wave whose loads are in flight together
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t bh = blockIdx.x;
   const int b = (int)(bh / a.Hq);
@@ -29,48 +32,64 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   const float4* ml = a.ml + bh * a.splits;
   const float* ap = a.ap + bh * a.splits * 2 * D;
 
-  __shared__ float sred[4];
-  __shared__ float sacc[4][2 * D + 2];
+  __shared__ float4 sst[4];
+  __shared__ float sacc[4][2 * D];
 
-  float mloc = kNegInf;
-  for (int s = threadIdx.x; s < ns; s += 256) mloc = fmaxf(mloc, ml[s].x);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-  if (lane == 0) sred[wave] = mloc;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
-
-  float l = 0.f, S = 0.f, A[DPL], P[DPL];
+  // Running state of this wave: max m, and l, S, A, P relative to it.
+  float m = kNegInf, l = 0.f, S = 0.f, A[DPL], P[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) { A[k] = 0.f; P[k] = 0.f; }
-#pragma unroll 4
-  for (int s = wave; s < ns; s += 4) {
-    const float4 st = ml[s];
-    const float* p = ap + (size_t)s * 2 * D + lane * DPL;
-    float av[DPL], pv[DPL];
+  for (int s0 = wave; s0 < ns; s0 += 4 * U) {
+    float4 st[U];
+    float av[U][DPL], pv[U][DPL];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) { av[k] = p[k]; pv[k] = p[D + k]; }
-    const float c = rescale(st.x, M);
-    l = fmaf(c, st.y, l);
-    S = fmaf(c, st.z, S);
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + 4 * u;
+      st[u] = s < ns ? ml[s] : make_float4(kNegInf, 0.f, 0.f, 0.f);
+      const float* p = ap + (size_t)min(s, ns - 1) * 2 * D + lane * DPL;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) { A[k] = fmaf(c, av[k], A[k]); P[k] = fmaf(c, pv[k], P[k]); }
+      for (int k = 0; k < DPL; ++k) { av[u][k] = p[k]; pv[u][k] = p[D + k]; }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + 4 * u >= ns) break;
+      const float mn = fmaxf(m, st[u].x);
+      const float cold = rescale(m, mn), cnew = rescale(st[u].x, mn);
+      m = mn;
+      l = l * cold + cnew * st[u].y;
+      S = S * cold + cnew * st[u].z;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        A[k] = A[k] * cold + cnew * av[u][k];
+        P[k] = P[k] * cold + cnew * pv[u][k];
+      }
+    }
   }
+  if (lane == 0) sst[wave] = make_float4(m, l, S, 0.f);
 #pragma unroll
   for (int k = 0; k < DPL; ++k) {
     sacc[wave][lane * DPL + k] = A[k];
     sacc[wave][D + lane * DPL + k] = P[k];
   }
-  if (lane == 0) { sacc[wave][2 * D] = l; sacc[wave][2 * D + 1] = S; }
   __syncthreads();
   if (wave == 0) {
-    const float lt = sacc[0][2 * D] + sacc[1][2 * D] + sacc[2][2 * D] + sacc[3][2 * D];
-    const float St = sacc[0][2 * D + 1] + sacc[1][2 * D + 1] + sacc[2][2 * D + 1] + sacc[3][2 * D + 1];
+    const float M = fmaxf(fmaxf(sst[0].x, sst[1].x), fmaxf(sst[2].x, sst[3].x));
+    float c[4], lt = 0.f, St = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      c[w] = rescale(sst[w].x, M);
+      lt += c[w] * sst[w].y;
+      St += c[w] * sst[w].z;
+    }
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {
       const int i = lane * DPL + k;
-      const float At = sacc[0][i] + sacc[1][i] + sacc[2][i] + sacc[3][i];
-      const float Pt = sacc[0][D + i] + sacc[1][D + i] + sacc[2][D + i] + sacc[3][D + i];
+      float At = 0.f, Pt = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        At += c[w] * sacc[w][i];
+        Pt += c[w] * sacc[w][D + i];
+      }
       store_output(a, bh * D + i, parallax_out(At, Pt, lt, St));
     }
   }

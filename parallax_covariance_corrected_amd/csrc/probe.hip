@@ -4,14 +4,16 @@
 //
 // As a matrix product: rho[B, N] = x[B, K] . W_R[N, K]^T with N = Hq*d and
 // K = d_model; both operands have K contiguous, which is exactly the operand
-// layout of the bf16 MFMA (8 consecutive K values per lane), so no transpose
-// or LDS staging of operands is needed. Products of bf16 values are exact in
-// fp32 and the accumulation is fp32.
+// layout of the bf16 MFMA (8 consecutive K values per lane), so neither needs
+// a transpose. Products of bf16 values are exact in fp32 and the accumulation
+// is fp32.
 //
 // bf16, small batch (B <= 64): a workgroup of NW waves owns a (16*MT rows) x
-// 16 columns tile; its waves split K NW ways, each issuing the loads of U
-// k-steps before their MFMAs, and reduce through LDS in a fixed order. Rows
-// past B read zeros (buffer range). Larger batches use an LDS-tiled GEMM.
+// 16 columns tile and loads its operands straight from memory into MFMA
+// registers; its waves split K NW ways, each issuing the loads of U k-steps
+// before their MFMAs, and reduce through LDS in a fixed order. Rows past B
+// read zeros (buffer range). Larger batches (B > 64): an LDS-tiled GEMM with
+// 128 x 128 tiles (below), where operand reuse across waves pays for staging.
 // fp32 kernel: one thread per output, a plain dot product.
 #include "common.h"
 
