@@ -183,6 +183,11 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
     const long long lo = wave_items ? 64 : 128;
     if (c < lo) c = lo;
     if (c > 2048) c = 2048;
+    // Short caches: one split. The merge launch costs a few microseconds
+    // whatever its size, more than the longer items cost here (measured: up
+    // to 22% faster at 256-512 keys and B <= 8; from 1024 keys on, splitting
+    // wins).
+    if (max_ctx <= 512) c = std::max<long long>(lo, (max_ctx + 63) / 64 * 64);
     chunk = (int)c;
   }
   p.chunk = chunk;

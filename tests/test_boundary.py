@@ -120,6 +120,9 @@ def test_plan_covers_context_and_picks_kernels():
     # about one workgroup per compute unit on the mid-context workload
     chunk, splits, _ = pb.decode_plan(16, 16, 8, 128, 4096)
     assert 16 * 8 * splits >= 256
+    # short caches take one split (no merge launch)
+    for B, ctx in ((1, 256), (8, 512), (2, 100)):
+        assert pb.decode_plan(B, 16, 8, 128, ctx)[1] == 1
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
