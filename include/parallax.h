@@ -136,16 +136,18 @@ int parallax_softmax_decode(const void* q, const void* k_cache, const void* v_ca
  * 0 .. P_b + t of KV head g = h / (Hq / Hkv). The caller has written the K/V
  * rows of the new tokens into the cache at P_b .. P_b + T - 1.
  *
- *   q           : [B, T, Hq, d]            bf16
+ *   q           : [B, T, Hq, d]            dtype storage (bf16 for both bf16 dtypes)
  *   rho         : [B, T, Hq, d]            fp32 (from parallax_probe on the B*T tokens)
- *   k_cache     : [B, Hkv, max_ctx, d]     bf16; rows >= P_b + T are never read
+ *   k_cache     : [B, Hkv, max_ctx, d]     dtype storage; rows >= P_b + T are never read
  *   v_cache     : [B, Hkv, max_ctx, d]     same layout as k_cache
  *   prefix_lens : [B] int32, device memory, or null; 0 <= P_b <= max_ctx - T
- *   out         : [B, T, Hq, d]            bf16 (PARALLAX_BF16) or fp32 (PARALLAX_BF16_F32OUT)
+ *   out         : [B, T, Hq, d]            bf16 (PARALLAX_BF16) or fp32 (the other dtypes)
  *
- * Requires 1 <= T <= max_ctx and the decode shape rules; PARALLAX_F32 is
- * UNSUPPORTED here. P_b outside 0 .. max_ctx - T is clamped on the device
- * (memory safety; a caller error). No workspace; enqueue-only on `stream`.
+ * Requires 1 <= T <= max_ctx and the decode shape rules. The bf16 dtypes run
+ * on the matrix cores; PARALLAX_F32 runs the vector-ALU decode kernel with one
+ * single-token sequence per token (a correctness path, not a fast one). P_b
+ * outside 0 .. max_ctx - T is clamped on the device (memory safety; a caller
+ * error). No workspace; enqueue-only on `stream`.
  */
 int parallax_prefill(const void* q, const float* rho, const void* k_cache, const void* v_cache,
                      const int* prefix_lens, void* out, int B, int T, int Hq, int Hkv, int d,

@@ -395,8 +395,6 @@ namespace {
 int prefill_impl(const void* q, const float* rho, const void* k_cache, const void* v_cache,
                  const int* prefix_lens, void* out, int B, int T, int Hq, int Hkv, int d,
                  int max_ctx, int dtype, hipStream_t stream) {
-  if (dtype == PARALLAX_F32)
-    return fail(PARALLAX_ERR_UNSUPPORTED, "prefill takes bf16 inputs (dtype BF16 or BF16_F32OUT)");
   int rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
   if (rc != PARALLAX_OK) return rc;
   if (T < 1 || T > max_ctx) return fail(PARALLAX_ERR_INVALID_ARG, "T must be in 1 .. max_ctx");
@@ -408,6 +406,36 @@ int prefill_impl(const void* q, const float* rho, const void* k_cache, const voi
   if (B > 65535 || Hkv > 65535 || (long long)T * (Hq / Hkv) > (1LL << 30) ||
       (long long)B * T * Hq > (1LL << 40))
     return fail(PARALLAX_ERR_UNSUPPORTED, "prefill size out of range");
+  if (dtype == PARALLAX_F32) {
+    // fp32: the vector-ALU decode kernel over B*T single-token "sequences"
+    // (token t of sequence b attends to rows 0 .. P_b + t), one split each.
+    if ((long long)B * T * Hkv * (Hq / Hkv) > 0x7fffffffLL)
+      return fail(PARALLAX_ERR_UNSUPPORTED, "prefill size out of range");
+    parallax::DecodeArgs g;
+    g.q = q;
+    g.rho = rho;
+    g.k = k_cache;
+    g.v = v_cache;
+    g.seq_lens = nullptr;
+    g.out = out;
+    g.ml = nullptr;
+    g.ap = nullptr;
+    g.B = B * T;
+    g.Hq = Hq;
+    g.Hkv = Hkv;
+    g.max_ctx = max_ctx;
+    g.chunk = max_ctx;
+    g.splits = 1;
+    g.out_f32 = 1;
+    g.scale_log2 = parallax::kLog2e / sqrtf((float)d);
+    g.T = T;
+    g.prefix = prefix_lens;
+    const parallax::LaunchEvents ev = profile_events();
+    hipError_t e = parallax::launch_decode_generic(g, d, 1, ev, stream);
+    profile_record(3, ev, e == hipSuccess);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return PARALLAX_OK;
+  }
   parallax::PrefillArgs a;
   a.q = q;
   a.rho = rho;

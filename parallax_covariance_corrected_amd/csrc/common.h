@@ -92,6 +92,11 @@ struct DecodeArgs {
   int splits;      // splits per (sequence, KV head)
   int out_f32;     // 1: out is fp32, 0: bf16
   float scale_log2;  // log2(e) / sqrt(d)
+  // Many-query (prefill) form of the generic kernel: when T > 0, sequence b of
+  // this call is token b % T of cache sequence b / T and attends to cache rows
+  // 0 .. prefix[b / T] + b % T (prefix may be null: 0); seq_lens is unused.
+  int T = 0;
+  const int* prefix = nullptr;
 };
 
 // Causal many-query forward: token t of sequence b is at cache position

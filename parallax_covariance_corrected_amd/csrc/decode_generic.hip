@@ -1,5 +1,6 @@
 // Generic vector-ALU Parallax decode kernel (fp32 or bf16 storage, d in {64, 128},
-// any GQA group). Serves the fp32 path and cross-checks the matrix-core kernel.
+// any GQA group). Serves the fp32 path (decode, and prefill with one "sequence"
+// per token) and cross-checks the matrix-core kernel.
 //
 // One workgroup (4 waves) per (split, sequence, KV head, head block). Each key
 // is read by LPK lanes with one 16-byte load of K and one of V; the lanes of a
@@ -67,7 +68,16 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   const int hb = unit_id % hblocks;
   const int kvh = (unit_id / hblocks) % a.Hkv;
   const int b = unit_id / hblocks / a.Hkv;
-  const int n = min(max(a.seq_lens[b], 0), a.max_ctx);
+  // Cache sequence and number of keys: decode reads seq_lens; the many-query
+  // form maps sequence b to token b % T of cache sequence b / T.
+  int cb = b, n;
+  if (a.T > 0) {
+    cb = b / a.T;
+    const int pre = min(max(a.prefix ? a.prefix[cb] : 0, 0), a.max_ctx - a.T);
+    n = pre + b % a.T + 1;
+  } else {
+    n = min(max(a.seq_lens[b], 0), a.max_ctx);
+  }
   const int c0 = split * a.chunk;
   if (split > 0 && c0 >= n) return;   // empty split (split 0 always runs: n = 0 -> out = 0)
   const int c1 = min(c0 + a.chunk, n);
@@ -95,7 +105,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
     for (int i = 0; i < EPL; ++i) { A[h][i] = 0.f; P[h][i] = 0.f; }
   }
 
-  const size_t seq = ((size_t)b * a.Hkv + kvh) * (size_t)a.max_ctx;
+  const size_t seq = ((size_t)cb * a.Hkv + kvh) * (size_t)a.max_ctx;
   const char* kb = (const char*)a.k + seq * ROW + sub * 16;
   const char* vb = (const char*)a.v + seq * ROW + sub * 16;
 

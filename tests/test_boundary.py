@@ -63,7 +63,7 @@ def _prefill(L, *, q=16, rho=16, k=16, v=16, pre=16, out=16, B=2, T=8, Hq=4, Hkv
 
 
 @pytest.mark.parametrize("kw,code,msg", [
-    (dict(dtype=pb.F32), pb.ERR_UNSUPPORTED, "bf16"),
+    (dict(dtype=9), pb.ERR_UNSUPPORTED, "dtype"),
     (dict(T=0), pb.ERR_INVALID_ARG, "T must"),
     (dict(T=65), pb.ERR_INVALID_ARG, "T must"),
     (dict(Hq=3, Hkv=2), pb.ERR_INVALID_ARG, "multiple"),

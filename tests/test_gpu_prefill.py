@@ -145,6 +145,26 @@ def test_prefill_full_size_sampled():
     assert e <= F32OUT_REL and a <= F32OUT_ABS
 
 
+@pytest.mark.parametrize("Hq,Hkv,d,T,prefix", [(2, 2, 64, 60, [0, 13]), (6, 2, 128, 33, [70, 0])])
+def test_fp32_prefill_matches_oracle(Hq, Hkv, d, T, prefix):
+    """fp32 inputs go through the vector-ALU kernel (one single-token
+    sequence per token): rel-L2 and max-abs within 1e-5, as for fp32 decode."""
+    wl = WORKLOADS[1].scaled(B=len(prefix), Hq=Hq, Hkv=Hkv, d=d, d_model=128)
+    s = make_prefill_inputs(wl, T, prefix, seed=2 * T)
+    say(f"[case] fp32 prefill Hq={Hq} Hkv={Hkv} d={d} T={T} prefix={prefix}")
+    rho = _rho(s)
+    ref = _oracle(s, rho)
+    o = _run(s, rho, torch.float32)
+    soft = pb.prefill(s.q.cuda(), None, padded_cache(s.K, s.max_ctx, device="cuda"),
+                      padded_cache(s.V, s.max_ctx, device="cuda"), s.prefix.cuda())
+    torch.cuda.synchronize()
+    ref0 = oracle.prefill(s.q, np.zeros_like(rho, dtype=np.float64), s.K, s.V, s.prefix.numpy(), Hkv)
+    say(f"fp32 prefill: rel {rel_l2(o, ref):.2e} abs {max_abs(o, ref):.2e}; "
+        f"softmax rel {rel_l2(to64(soft), ref0):.2e}")
+    assert rel_l2(o, ref) <= 1e-5 and max_abs(o, ref) <= 1e-5
+    assert rel_l2(to64(soft), ref0) <= 1e-5
+
+
 def test_prefill_rejects_bad_arguments():
     wl = WORKLOADS[2].scaled(B=1, Hq=4, Hkv=2, d=128, d_model=256)
     s = make_prefill_inputs(wl, 8, [0], seed=0)
@@ -152,6 +172,6 @@ def test_prefill_rejects_bad_arguments():
     rho = torch.zeros((1, 8, 4, 128), device="cuda")
     K = padded_cache(s.K, 8, device="cuda")
     with pytest.raises(pb.ParallaxError):
-        pb.prefill(q.float(), rho, K.float(), K.float())       # fp32 inputs: unsupported
-    with pytest.raises(pb.ParallaxError):
         pb.prefill(q, rho, K[:, :, :4].contiguous(), K[:, :, :4].contiguous())   # T > max_ctx
+    with pytest.raises(ValueError):
+        pb.prefill(q, rho, K.float(), K.float())      # mixed dtypes
