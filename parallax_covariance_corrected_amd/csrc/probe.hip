@@ -22,21 +22,25 @@ namespace {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-template <int MT, int NT, int NW, int U>
+// COLS < 16 (with NT = 1): the workgroup owns only COLS output columns (the
+// other MFMA columns read zeros), so twice as many workgroups share the W_R
+// stream (measured 8% faster at B = 16, d_model = 2048).
+template <int MT, int NT, int NW, int U, int COLS = 16 * NT>
 __global__ __launch_bounds__(NW * 64) void probe_mfma_kernel(const uint16_t* __restrict__ W,
                                                              const uint16_t* __restrict__ x,
                                                              float* __restrict__ rho, int B, int N,
                                                              int K) {
+  static_assert(COLS == 16 * NT || (NT == 1 && COLS < 16), "narrow tiles are single MFMA tiles");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * 16 * NT;
+  const int n0 = blockIdx.x * COLS;
   const int m0 = blockIdx.y * 16 * MT;
   const unsigned rowb = (unsigned)K * 2;
-  // x rows m0.. (rows >= B read as zero), W rows n0..
+  // x rows m0.. (rows >= B read as zero), W rows n0.. n0 + COLS - 1
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (size_t)m0 * K,
                                               (unsigned)(min(B - m0, 16 * MT)) * rowb);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + (size_t)n0 * K,
-                                              (unsigned)(min(N - n0, 16 * NT)) * rowb);
+                                              (unsigned)(min(N - n0, COLS)) * rowb);
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
@@ -56,7 +60,9 @@ __global__ __launch_bounds__(NW * 64) void probe_mfma_kernel(const uint16_t* __r
 #pragma unroll
       for (int i = 0; i < MT; ++i) xa[u][i] = buf_load16(xr, (unsigned)(16 * i + l16) * rowb + koff);
 #pragma unroll
-      for (int jn = 0; jn < NT; ++jn) wb[u][jn] = buf_load16(wr, (unsigned)(16 * jn + l16) * rowb + koff);
+      for (int jn = 0; jn < NT; ++jn)
+        wb[u][jn] = buf_load16(wr, 16 * jn + l16 < COLS ? (unsigned)(16 * jn + l16) * rowb + koff
+                                                        : 0x80000000u);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -91,7 +97,7 @@ __global__ __launch_bounds__(NW * 64) void probe_mfma_kernel(const uint16_t* __r
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = m0 + 16 * i + 4 * grp + r;
-          if (row < B && col < N) rho[(size_t)row * N + col] = v[r];
+          if (16 * jn + l16 < COLS && row < B && col < N) rho[(size_t)row * N + col] = v[r];
         }
       }
   }
@@ -240,7 +246,10 @@ hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, 
     const int mt = (B + 15) / 16;
     dim3 grid((N + 15) / 16, 1);
     switch (mt) {
-      case 1: hipExtLaunchKernelGGL((probe_mfma_kernel<1, 1, 8, 8>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K); break;
+      case 1:
+        grid.x = (N + 7) / 8;
+        hipExtLaunchKernelGGL((probe_mfma_kernel<1, 1, 8, 8, 8>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
+        break;
       case 2: hipExtLaunchKernelGGL((probe_mfma_kernel<2, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K); break;
       case 3: hipExtLaunchKernelGGL((probe_mfma_kernel<3, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K); break;
       default: hipExtLaunchKernelGGL((probe_mfma_kernel<4, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K); break;
