@@ -147,6 +147,60 @@ def matched_ratios(pb, wl, dev_sets, reps: int):
             "compute_matched_speedup": round(t_soft2 / t_par, 4)}
 
 
+def read_ceiling(pb, reps: int = 30):
+    """Rate of the library's read reference (the decode's K load shape) over
+    three rotated 256 MiB buffers: a read-only ceiling measured on this GPU."""
+    import torch
+    n = 256 << 20
+    bufs = [torch.full((n,), i + 1, dtype=torch.uint8, device="cuda") for i in range(3)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for i in range(3):
+        pb.read_bandwidth(bufs[i], sink)
+    torch.cuda.synchronize()
+    pb.profile_reset()
+    with pb.options(profile=1):
+        for i in range(reps):
+            pb.read_bandwidth(bufs[i % 3], sink)
+        torch.cuda.synchronize()
+    ms, cnt = pb.profile_read(pb.KERNEL_READ)
+    del bufs
+    torch.cuda.empty_cache()
+    return n / (ms / cnt * 1e-3) / 1e9
+
+
+def step_percentiles(pb, wl, dev_sets, reps: int):
+    """p10 / p50 / p90 of single-step times (each step bracketed by its own
+    events), cold (rotated input sets) and warm (one set repeated)."""
+    import torch
+
+    def times(pick):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            step(pb, wl, pick(i))
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        return [round(t[int(q * (reps - 1))], 2) for q in (0.1, 0.5, 0.9)]
+
+    cold = times(lambda i: dev_sets[i % len(dev_sets)])
+    for _ in range(5):
+        step(pb, wl, dev_sets[0])
+    warm = times(lambda i: dev_sets[0])
+    return {"cold_p10_p50_p90_us": cold, "warm_p10_p50_p90_us": warm}
+
+
+def correction_ratio(pb, d):
+    """||C rho|| / ||out||: the share of the correction in the output, from the
+    Parallax and softmax-only outputs of the same kernels on the same inputs."""
+    import torch
+    par = pb.decode(d["q"], d["rho"], d["K"], d["V"], d["seq_lens"], out_dtype=torch.float32)
+    soft = pb.softmax_decode(d["q"], d["K"], d["V"], d["seq_lens"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return round(float((par - soft).norm() / par.norm()), 4)
+
+
 def run_workload(args, wl_id: int, emit: bool = True):
     import torch
     from parallax_covariance_corrected_amd import binding as pb
@@ -226,8 +280,14 @@ def run_workload(args, wl_id: int, emit: bool = True):
                      "probe_avg_us": round(prb_ms / max(prb_n, 1) * 1e3, 3)},
         "cpu_baseline": None,
     }
+    rec["step_time_distribution"] = step_percentiles(pb, wl, dev_sets, args.steps)
     if wl.dtype == "bf16":
         rec["matched"] = matched_ratios(pb, wl, dev_sets, args.steps)
+        step(pb, wl, dev_sets[0])
+        rec["correction_to_output"] = correction_ratio(pb, dev_sets[0])
+        ceiling = read_ceiling(pb)
+        rec["roofline"]["read_ceiling_gbps"] = round(ceiling, 1)
+        rec["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling, 4)
     if args.cpu_baseline:
         print("# bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(sets_host[0])

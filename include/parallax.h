@@ -202,12 +202,25 @@ int parallax_get_option(int option, int* value);
  * Kernel timing when PARALLAX_OPT_PROFILE is 1: every launch carries start and
  * stop HIP events stamped by its own dispatch (hipExtLaunchKernel), so the
  * timing adds no work between kernels. kernel: 0 = probe, 1 = decode
- * (split-K pass), 2 = merge, 3 = prefill.
+ * (split-K pass), 2 = merge, 3 = prefill, 4 = the read reference below.
  * parallax_profile_read waits for the recorded events and returns the summed
  * duration (ms) and the number of launches since the last reset.
  */
 int parallax_profile_read(int kernel, double* total_ms, long long* launches);
 int parallax_profile_reset(void);
+
+/*
+ * parallax_read_bandwidth — a measurement hook, not part of the method: reads
+ * `bytes` of device memory at `buf` once, with the load shape the decode kernel
+ * uses for K (non-temporal 16-byte loads, eight in flight per lane, 256
+ * workgroups each streaming a contiguous share), so that the decode's HBM rate
+ * can be stated against a rate this machine reaches as well as the nominal
+ * peak. bytes: a positive multiple of 1 MiB, below 512 GiB; buf 16-byte
+ * aligned; sink: 4 bytes of device memory the kernel may write (it keeps the
+ * loads from being optimised away). Enqueue-only on `stream`; time it with
+ * PARALLAX_OPT_PROFILE (kernel 4).
+ */
+int parallax_read_bandwidth(const void* buf, long long bytes, unsigned* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

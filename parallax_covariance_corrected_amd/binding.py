@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_MEMORY = 0, 1, 2, 3, 4
 F32, BF16, BF16_F32OUT = 0, 1, 2
 OPT_CHUNK, OPT_KERNEL, OPT_PROFILE, OPT_ITEMS = 1, 2, 3, 4
-KERNEL_PROBE, KERNEL_DECODE, KERNEL_MERGE, KERNEL_PREFILL = 0, 1, 2, 3
+KERNEL_PROBE, KERNEL_DECODE, KERNEL_MERGE, KERNEL_PREFILL, KERNEL_READ = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -45,6 +45,7 @@ def lib() -> ctypes.CDLL:
         L.parallax_softmax_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
         L.parallax_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
         L.parallax_softmax_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+        L.parallax_read_bandwidth.argtypes = [vp, ctypes.c_longlong, vp, vp]
         L.parallax_decode_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i),
                                            ctypes.POINTER(i), ctypes.POINTER(i)]
         L.parallax_set_option.argtypes = [i, i]
@@ -53,7 +54,8 @@ def lib() -> ctypes.CDLL:
                                             ctypes.POINTER(ctypes.c_longlong)]
         L.parallax_profile_reset.argtypes = []
         for name in ("parallax_probe", "parallax_decode", "parallax_softmax_decode",
-                     "parallax_prefill", "parallax_softmax_prefill", "parallax_decode_plan",
+                     "parallax_prefill", "parallax_softmax_prefill", "parallax_read_bandwidth",
+                     "parallax_decode_plan",
                      "parallax_set_option", "parallax_get_option", "parallax_profile_read",
                      "parallax_profile_reset"):
             getattr(L, name).restype = i
@@ -195,6 +197,16 @@ def prefill(q: torch.Tensor, rho: Optional[torch.Tensor], k_cache: torch.Tensor,
         _check(lib().parallax_prefill(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), pp,
                                       _ptr(out), B, T, Hq, Hkv, d, max_ctx, code, _stream()))
     return out
+
+
+def read_bandwidth(buf: torch.Tensor, sink: torch.Tensor):
+    """Measurement hook: stream `buf` (contiguous, device, size a multiple of
+    1 MiB) once with the decode's load shape; time it with options(profile=1)
+    and profile_read(KERNEL_READ)."""
+    _need(buf, "buf")
+    _need(sink, "sink")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().parallax_read_bandwidth(_ptr(buf), nbytes, _ptr(sink), _stream()))
 
 
 def decode_plan(B: int, Hq: int, Hkv: int, d: int, max_ctx: int, dtype: int = BF16):

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libparallax.so")
 SOURCES = ["api.hip", "decode_mfma.hip", "decode_generic.hip", "merge.hip", "probe.hip",
-           "prefill_mfma.hip"]
+           "prefill_mfma.hip", "readbench.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled: the compiler would otherwise emit them

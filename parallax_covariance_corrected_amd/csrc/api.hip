@@ -13,6 +13,11 @@
 #include "../../include/parallax.h"
 #include "common.h"
 
+namespace parallax {
+hipError_t launch_read_stream(const void* buf, size_t bytes, int grid, unsigned* sink,
+                              LaunchEvents ev, hipStream_t s);
+}
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -43,7 +48,7 @@ struct Timing {
   long long launches = 0;
 };
 std::mutex g_prof_mu;
-Timing g_prof[4];   // probe, decode, merge, prefill
+Timing g_prof[5];   // probe, decode, merge, prefill, read reference
 std::vector<hipEvent_t> g_event_pool;
 
 hipEvent_t take_event() {
@@ -253,7 +258,7 @@ int parallax_profile_reset(void) {
 }
 
 int parallax_profile_read(int kernel, double* total_ms, long long* launches) {
-  if (kernel < 0 || kernel > 3) return fail(PARALLAX_ERR_INVALID_ARG, "kernel must be 0, 1, 2 or 3");
+  if (kernel < 0 || kernel > 4) return fail(PARALLAX_ERR_INVALID_ARG, "kernel must be 0 .. 4");
   if (!total_ms || !launches) return fail(PARALLAX_ERR_INVALID_ARG, "null output pointer");
   std::lock_guard<std::mutex> g(g_prof_mu);
   Timing& t = g_prof[kernel];
@@ -474,6 +479,25 @@ int parallax_softmax_prefill(const void* q, const void* k_cache, const void* v_c
                              int d, int max_ctx, int dtype, hipStream_t stream) {
   return prefill_impl(q, nullptr, k_cache, v_cache, prefix_lens, out, B, T, Hq, Hkv, d, max_ctx,
                       dtype, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int parallax_read_bandwidth(const void* buf, long long bytes, unsigned* sink, hipStream_t stream) {
+  constexpr int kGrid = 256;
+  if (!buf || !sink) return fail(PARALLAX_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(buf, 16) || !aligned(sink, 4))
+    return fail(PARALLAX_ERR_INVALID_ARG, "buf must be 16-byte aligned (sink 4-byte)");
+  if (bytes <= 0 || bytes % ((long long)kGrid * 4096) != 0 || bytes / kGrid >= (1LL << 31))
+    return fail(PARALLAX_ERR_INVALID_ARG,
+                "bytes must be a positive multiple of 1 MiB and below 512 GiB");
+  const parallax::LaunchEvents ev = profile_events();
+  hipError_t e = parallax::launch_read_stream(buf, (size_t)bytes, kGrid, sink, ev, stream);
+  profile_record(4, ev, e == hipSuccess);
+  if (e != hipSuccess) return hip_fail(e, "read launch");
+  return PARALLAX_OK;
 }
 
 }  // extern "C"

@@ -79,6 +79,14 @@ def test_prefill_rejects_bad_arguments(L, kw, code, msg):
     assert msg in L.parallax_last_error().decode()
 
 
+def test_read_bandwidth_rejects_bad_arguments(L):
+    assert L.parallax_read_bandwidth(0, 1 << 20, 16, None) == pb.ERR_INVALID_ARG
+    assert L.parallax_read_bandwidth(24, 1 << 20, 16, None) == pb.ERR_INVALID_ARG
+    assert L.parallax_read_bandwidth(16, (1 << 20) + 4096, 16, None) == pb.ERR_INVALID_ARG
+    assert L.parallax_read_bandwidth(16, 0, 16, None) == pb.ERR_INVALID_ARG
+    assert "1 MiB" in L.parallax_last_error().decode()
+
+
 def test_softmax_decode_rejects_bad_arguments(L):
     assert L.parallax_softmax_decode(16, 16, 16, 16, 16, 2, 3, 2, 128, 64, pb.BF16, None) == pb.ERR_INVALID_ARG
     assert L.parallax_softmax_decode(0, 16, 16, 16, 16, 2, 4, 2, 128, 64, pb.BF16, None) == pb.ERR_INVALID_ARG
