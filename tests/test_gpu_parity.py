@@ -116,14 +116,21 @@ EDGE_LENS = [0, 1, 15, 16, 17, 127, 128, 129, 300]
 
 @pytest.mark.parametrize("d,Hq,Hkv,dtype", [(128, 4, 2, "bf16"), (64, 6, 2, "bf16"),
                                             (128, 16, 2, "bf16"), (64, 3, 3, "bf16"),
+                                            (128, 32, 2, "bf16"), (64, 20, 4, "bf16"),
+                                            (128, 12, 2, "bf16"),
                                             (128, 4, 2, "f32"), (64, 2, 1, "f32")])
 def test_edge_lengths(d, Hq, Hkv, dtype):
+    """Lengths 0, 1, tile and chunk boundaries, max; G in {1, 2, 3, 5, 6, 8, 16}
+    (head blocks of 1 to 4 query heads). bf16 runs on the default plan (one
+    split at this cache size) and with 128-key chunks (three splits + merge)."""
     wl = WORKLOADS[2].scaled(B=len(EDGE_LENS), Hq=Hq, Hkv=Hkv, d=d, ctx=300, d_model=256,
                              dtype=dtype, wr_std=0.05)
     s = make_inputs(wl, 3, lengths=EDGE_LENS)
     tag = f"edge d={d} Hq={Hq} Hkv={Hkv} {dtype}"
     if dtype == "bf16":
         _run_full_check(s, tag)
+        with pb.options(chunk=128):
+            _run_full_check(s, tag + " chunk=128", wr_zero_too=False)
         return
     say(f"[case] {tag}")
     dev = Device(s)
