@@ -58,7 +58,7 @@ CASES = [  # (Hq, Hkv, d, T, prefix)
     (8, 1, 64, 40, [0, 130]),       # G = 8
     (2, 2, 64, 97, [0, 1]),         # G = 1
     (4, 2, 64, 150, [64, 0]),
-    (32, 8, 128, 100, [0, 300]),    # G = 4 (the ragged workload's heads)
+    (32, 8, 128, 40, [0, 150]),     # G = 4 (the ragged workload's heads)
     (12, 2, 64, 45, [7, 0]),        # G = 6
 ]
 
