@@ -187,12 +187,17 @@ int parallax_decode_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
  *   PARALLAX_OPT_PROFILE : 1 = record HIP events around every kernel launch
  *   PARALLAX_OPT_ITEMS   : matrix-core work items: 0 = automatic,
  *                          1 = four waves per item, 2 = one wave per item
+ *   PARALLAX_OPT_ORDER   : numbering of four-wave work items: 0 = automatic,
+ *                          1 = every (split, sequence, head) item, split-major,
+ *                          2 = only the non-empty ones (up to 256 sequences and
+ *                          64 splits; otherwise as 1)
  */
 typedef enum {
   PARALLAX_OPT_CHUNK = 1,
   PARALLAX_OPT_KERNEL = 2,
   PARALLAX_OPT_PROFILE = 3,
-  PARALLAX_OPT_ITEMS = 4
+  PARALLAX_OPT_ITEMS = 4,
+  PARALLAX_OPT_ORDER = 5
 } parallax_option;
 
 int parallax_set_option(int option, int value);

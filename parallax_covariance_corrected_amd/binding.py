@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_MEMORY = 0, 1, 2, 3, 4
 F32, BF16, BF16_F32OUT = 0, 1, 2
-OPT_CHUNK, OPT_KERNEL, OPT_PROFILE, OPT_ITEMS = 1, 2, 3, 4
+OPT_CHUNK, OPT_KERNEL, OPT_PROFILE, OPT_ITEMS, OPT_ORDER = 1, 2, 3, 4, 5
 KERNEL_PROBE, KERNEL_DECODE, KERNEL_MERGE, KERNEL_PREFILL, KERNEL_READ = 0, 1, 2, 3, 4
 
 _lib = None
@@ -243,7 +243,7 @@ class options:
 
     def __init__(self, **kw):
         self.kw = {{"chunk": OPT_CHUNK, "kernel": OPT_KERNEL, "profile": OPT_PROFILE,
-                    "items": OPT_ITEMS}[k]: v
+                    "items": OPT_ITEMS, "order": OPT_ORDER}[k]: v
                    for k, v in kw.items()}
         self.saved = {}
 

@@ -38,6 +38,7 @@ int g_opt_chunk = 0;
 int g_opt_kernel = 0;
 int g_opt_profile = 0;
 int g_opt_items = 0;
+int g_opt_order = 0;
 
 // ---------------------------------------------------------------- profiling
 // Start/stop events are handed to hipExtLaunchKernel, which stamps them from
@@ -135,6 +136,7 @@ struct Plan {
   int chunk;
   int splits;
   int kernel;   // 1 generic, 2 matrix-core workgroup items, 3 matrix-core wave items
+  int compact;  // 1: compacted item numbering (kernel 2 only)
 };
 
 int esize(int dtype) { return dtype == PARALLAX_F32 ? 4 : 2; }
@@ -197,6 +199,17 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
   }
   p.chunk = chunk;
   p.splits = (max_ctx + chunk - 1) / chunk;
+  // Several sequences in a cache of many chunks: lengths may differ, leaving
+  // empty items among the working ones; number only the non-empty ones (the
+  // kernel reads the lengths; up to 256 sequences and 64 splits). Measured on
+  // a log-uniform ragged batch (64 sequences, 32768-key cache): 9-25% faster
+  // decode. Each workgroup then finds its item from all the lengths before its
+  // first load, about 1 us that only pays off when the grid has several
+  // workgroups per compute unit.
+  const bool can_compact = p.kernel == 2 && B <= 256 && p.splits <= 64;
+  p.compact = can_compact && B >= 2 && p.splits >= 3 && units * p.splits >= 1024;
+  if (g_opt_order == 1) p.compact = 0;
+  if (g_opt_order == 2) p.compact = can_compact;
   return p;
 }
 
@@ -225,6 +238,10 @@ int parallax_set_option(int option, int value) {
       if (value < 0 || value > 2) return fail(PARALLAX_ERR_INVALID_ARG, "items must be 0, 1 or 2");
       g_opt_items = value;
       return PARALLAX_OK;
+    case PARALLAX_OPT_ORDER:
+      if (value < 0 || value > 2) return fail(PARALLAX_ERR_INVALID_ARG, "order must be 0, 1 or 2");
+      g_opt_order = value;
+      return PARALLAX_OK;
 
     default:
       return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
@@ -238,6 +255,7 @@ int parallax_get_option(int option, int* value) {
     case PARALLAX_OPT_KERNEL: *value = g_opt_kernel; return PARALLAX_OK;
     case PARALLAX_OPT_PROFILE: *value = g_opt_profile; return PARALLAX_OK;
     case PARALLAX_OPT_ITEMS: *value = g_opt_items; return PARALLAX_OK;
+    case PARALLAX_OPT_ORDER: *value = g_opt_order; return PARALLAX_OK;
     default: return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
   }
 }
@@ -361,7 +379,7 @@ int decode_impl(const void* q, const float* rho, const void* k_cache, const void
   parallax::LaunchEvents ev = profile_events();
   hipError_t e =
       (p.kernel >= 2)
-          ? parallax::launch_decode_mfma(a, d, p.kernel == 3 ? 1 : 0, ev, stream)
+          ? parallax::launch_decode_mfma(a, d, p.kernel == 3 ? 1 : 0, p.compact, ev, stream)
           : parallax::launch_decode_generic(a, d, dtype == PARALLAX_F32 ? 1 : 0, ev, stream);
   profile_record(1, ev, e == hipSuccess);
   if (e == hipSuccess && p.splits > 1) {

@@ -131,8 +131,9 @@ struct LaunchEvents {
 // Internal launchers (one translation unit each). Return hipError_t.
 hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, LaunchEvents ev,
                                  hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, LaunchEvents ev,
-                              hipStream_t s);
+// compact = 1: compacted item numbering (workgroup items, B <= 256 only).
+hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, int compact,
+                              LaunchEvents ev, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, int d, LaunchEvents ev, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int d, LaunchEvents ev, hipStream_t s);
 bool decode_mfma_supported(int d, int G);

@@ -17,6 +17,12 @@
 //  * workgroup items (long contexts): the 4 waves of a workgroup take
 //    interleaved 16-key tiles of one item and merge their states in LDS;
 //  * wave items (short contexts, many sequences): every wave owns one item.
+// With a ragged batch in a large cache many split-major items are empty (the
+// split starts past the sequence's end). In the compacted numbering
+// (workgroup items, up to 256 sequences) workgroup i takes the i-th non-empty
+// item of the split-major order instead, so the workgroups that find nothing
+// form one run at the end of the grid rather than being interleaved with
+// working ones.
 // A sequence that fits in one chunk gets its output written directly;
 // otherwise each non-empty split writes its partial state (m, l, S, A, P)
 // and the merge kernel combines them.
@@ -126,7 +132,65 @@ __device__ __forceinline__ void pv_tile(const typename KV<D>::Tile& tl, const fl
   (pv_key<D, NSET, KK>(tl, w0, w1, acc), ...);
 }
 
-template <int D, int GH, bool WAVE_ITEM, int NW, bool CORR>
+// Compacted numbering: item `item` of the call is the item-th non-empty
+// (split, unit) pair in split-major order, where a unit is one of the `ups`
+// (KV head, head block) pairs of a sequence and split s >= 1 of sequence b is
+// non-empty when it starts before the sequence's end (split 0 always runs).
+// Every wave of the workgroup computes the same answer from the B lengths
+// (B <= 64 * kCompactGroups); returns false when the item does not exist.
+constexpr int kCompactGroups = 4;
+__device__ __forceinline__ bool compact_item(const DecodeArgs& a, int item, int ups, int& split,
+                                             int& unit_id) {
+  const int lane = threadIdx.x & 63;
+  const int groups = (a.B + 63) >> 6;
+  int n[kCompactGroups];
+  int mine = 0;   // non-empty splits of this lane's sequences
+#pragma unroll
+  for (int g = 0; g < kCompactGroups; ++g) {
+    const int b = 64 * g + lane;
+    n[g] = b < a.B ? min(max(a.seq_lens[b], 0), a.max_ctx) : -1;
+    if (n[g] >= 0) mine += max(1, (n[g] + a.chunk - 1) / a.chunk);
+  }
+  // Workgroups past the last non-empty item leave at once.
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o);
+  if (item >= mine * ups) return false;
+  int base = 0;
+  for (int s = 0; s < a.splits; ++s) {
+    const int lo = s * a.chunk;
+    unsigned long long m[kCompactGroups];
+    int cnt = 0;
+#pragma unroll
+    for (int g = 0; g < kCompactGroups; ++g) {
+      m[g] = g < groups ? __ballot(s == 0 ? n[g] >= 0 : n[g] > lo) : 0ull;
+      cnt += __popcll(m[g]);
+    }
+    const int span = cnt * ups;
+    if (item < base + span) {
+      int r = (item - base) / ups;
+      const int within = (item - base) - r * ups;
+#pragma unroll
+      for (int g = 0; g < kCompactGroups; ++g) {
+        const int c = __popcll(m[g]);
+        if (r < c) {
+          // the lane holding the r-th set bit of m[g]
+          const unsigned below = __builtin_amdgcn_mbcnt_hi(
+              (unsigned)(m[g] >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m[g], 0u));
+          const unsigned long long hit = __ballot(((m[g] >> lane) & 1ull) && (int)below == r);
+          const int b = 64 * g + __builtin_ctzll(hit);
+          split = __builtin_amdgcn_readfirstlane(s);
+          unit_id = __builtin_amdgcn_readfirstlane(b * ups + within);
+          return true;
+        }
+        r -= c;
+      }
+    }
+    base += span;
+  }
+  return false;
+}
+
+template <int D, int GH, bool WAVE_ITEM, int NW, bool CORR, bool COMPACT>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   using L = Layout<GH, CORR>;
   using C = KV<D>;
@@ -140,8 +204,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const int units = a.B * a.Hkv * hblocks;
   int item = WAVE_ITEM ? blockIdx.x * NW + wave : blockIdx.x;
   if (WAVE_ITEM && item >= units * a.splits) return;
-  const int split = item / units;
-  const int unit_id = item - split * units;
+  int split, unit_id;
+  if constexpr (COMPACT) {
+    static_assert(!WAVE_ITEM, "compacted numbering is for workgroup items");
+    if (!compact_item(a, item, units / a.B, split, unit_id)) return;
+  } else {
+    split = item / units;
+    unit_id = item - split * units;
+  }
   const int hb = unit_id % hblocks;
   const int kvh = (unit_id / hblocks) % a.Hkv;
   const int b = unit_id / hblocks / a.Hkv;
@@ -412,7 +482,7 @@ int head_block(int G) {
   return 1;
 }
 
-template <int D, bool WI, int NW, bool CORR>
+template <int D, bool WI, int NW, bool CORR, bool CP>
 hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int GH = head_block(G);
@@ -421,29 +491,37 @@ hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   if (grid > 0x7fffffffu || items > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), blk(NW * 64);
   switch (GH) {
-    case 4: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 4, WI, NW, CORR>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 3: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 3, WI, NW, CORR>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 2, WI, NW, CORR>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 1, WI, NW, CORR>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 4, WI, NW, CORR, CP>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 3: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 3, WI, NW, CORR, CP>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 2, WI, NW, CORR, CP>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 1, WI, NW, CORR, CP>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
   }
   return hipGetLastError();
 }
 
 template <bool CORR>
-hipError_t launch_d(const DecodeArgs& a, int d, int wave_items, LaunchEvents ev, hipStream_t s) {
+hipError_t launch_d(const DecodeArgs& a, int d, int wave_items, int compact, LaunchEvents ev,
+                    hipStream_t s) {
   if (wave_items)
-    return d == 64 ? launch_dw<64, true, 4, CORR>(a, ev, s) : launch_dw<128, true, 4, CORR>(a, ev, s);
-  return d == 64 ? launch_dw<64, false, 4, CORR>(a, ev, s) : launch_dw<128, false, 4, CORR>(a, ev, s);
+    return d == 64 ? launch_dw<64, true, 4, CORR, false>(a, ev, s)
+                   : launch_dw<128, true, 4, CORR, false>(a, ev, s);
+  if (compact)
+    return d == 64 ? launch_dw<64, false, 4, CORR, true>(a, ev, s)
+                   : launch_dw<128, false, 4, CORR, true>(a, ev, s);
+  return d == 64 ? launch_dw<64, false, 4, CORR, false>(a, ev, s)
+                 : launch_dw<128, false, 4, CORR, false>(a, ev, s);
 }
 
 }  // namespace
 
 bool decode_mfma_supported(int d, int G) { return (d == 64 || d == 128) && G >= 1; }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, LaunchEvents ev,
-                              hipStream_t s) {
+hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, int compact,
+                              LaunchEvents ev, hipStream_t s) {
+  if (compact && (wave_items || a.B > 64 * kCompactGroups)) return hipErrorInvalidValue;
   // rho == nullptr selects plain softmax attention (no correction branch).
-  return a.rho ? launch_d<true>(a, d, wave_items, ev, s) : launch_d<false>(a, d, wave_items, ev, s);
+  return a.rho ? launch_d<true>(a, d, wave_items, compact, ev, s)
+               : launch_d<false>(a, d, wave_items, compact, ev, s);
 }
 
 }  // namespace parallax

@@ -100,12 +100,16 @@ def test_options_and_profile_on_host(L):
     assert L.parallax_set_option(pb.OPT_CHUNK, 100) == pb.ERR_INVALID_ARG
     assert L.parallax_set_option(pb.OPT_ITEMS, 3) == pb.ERR_INVALID_ARG
     assert L.parallax_set_option(99, 0) == pb.ERR_INVALID_ARG
+    assert L.parallax_set_option(pb.OPT_ORDER, 3) == pb.ERR_INVALID_ARG
     with pb.options(chunk=512, kernel=1):
         assert pb.get_option(pb.OPT_CHUNK) == 512 and pb.get_option(pb.OPT_KERNEL) == 1
         assert pb.decode_plan(16, 16, 8, 128, 4096) == (512, 8, 1)
     with pb.options(items=2, chunk=256):
         assert pb.decode_plan(16, 16, 8, 128, 4096) == (256, 16, 3)
+    with pb.options(order=2):
+        assert pb.get_option(pb.OPT_ORDER) == 2
     assert pb.get_option(pb.OPT_CHUNK) == 0 and pb.get_option(pb.OPT_KERNEL) == 0
+    assert pb.get_option(pb.OPT_ORDER) == 0
     pb.profile_reset()
     assert pb.profile_read(pb.KERNEL_DECODE) == (0.0, 0)
     with pytest.raises(pb.ParallaxError):

@@ -176,6 +176,35 @@ def test_split_and_kernel_invariance(chunk, kernel, items):
     assert rel_l2(o32, ref) <= 1e-5 and max_abs(o32, ref) <= 1e-4
 
 
+@pytest.mark.parametrize("B", [70, 130])
+def test_compacted_item_order_matches_split_major(B):
+    """Numbering only the non-empty work items (a ragged batch in a cache of
+    many chunks; sequences in two or three groups of 64) computes the same
+    items as the split-major numbering of every item: equal bit for bit, and
+    right against the oracle when the workspace still holds another input's
+    partial states (an item left out would leave one of those behind)."""
+    wl = WORKLOADS[5].scaled(B=B, Hq=8, Hkv=2, ctx=2000, d_model=256)
+    r = np.random.default_rng(B)
+    lens = [0, 1, 255, 256, 257, 2000] + [int(x) for x in r.integers(0, 2001, B - 6)]
+    s = make_inputs(wl, 21, lengths=lens)
+    other = make_inputs(wl, 22, lengths=[2000] * B)
+    say(f"[case] compacted order B={B} chunk=256")
+    dev, dev2 = Device(s), Device(other)
+    rho, rho2 = dev.probe(), dev2.probe()
+    with pb.options(chunk=256, order=1, items=1):
+        plain = to64(dev.decode(rho, out_dtype=torch.float32))
+    with pb.options(chunk=256, order=2, items=1):
+        dev2.decode(rho2, out_dtype=torch.float32)
+        comp = to64(dev.decode(rho, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(comp, plain)
+    pairs = sample_pairs(s, 24) + [(0, 0), (1, 3), (5, 7), (B - 1, 7)]
+    ref = oracle_out(s, oracle_rho(s), pairs)
+    got = np.stack([comp[b, h] for b, h in pairs])
+    say(f"compacted B={B}: rel {rel_l2(got, ref):.3e} max_abs {max_abs(got, ref):.3e}")
+    assert rel_l2(got, ref) <= 1e-5 and max_abs(got, ref) <= 1e-4
+
+
 def test_gqa_equals_replicated_mha():
     wl = WORKLOADS[2].scaled(B=2, ctx=700, d_model=128)
     s = make_inputs(wl, 4, lengths=[700, 333])
