@@ -243,16 +243,25 @@ hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, 
     dim3 grid((N + kGN - 1) / kGN, (B + kGM - 1) / kGM);
     hipExtLaunchKernelGGL(probe_gemm_kernel, grid, dim3(kGThreads), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
   } else {
+    // Shapes picked by a sweep over cold W_R (tiles of 8 / 16 columns, 4-16
+    // waves, 2-8 k-steps in flight): aim for at least 256 workgroups, since a
+    // workgroup's read of its W_R rows is latency-bound.
     const int mt = (B + 15) / 16;
     dim3 grid((N + 15) / 16, 1);
-    switch (mt) {
-      case 1:
-        grid.x = (N + 7) / 8;
-        hipExtLaunchKernelGGL((probe_mfma_kernel<1, 1, 8, 8, 8>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
-        break;
-      case 2: hipExtLaunchKernelGGL((probe_mfma_kernel<2, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K); break;
-      case 3: hipExtLaunchKernelGGL((probe_mfma_kernel<3, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K); break;
-      default: hipExtLaunchKernelGGL((probe_mfma_kernel<4, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K); break;
+    if (mt == 1) {
+      grid.x = (N + 7) / 8;
+      hipExtLaunchKernelGGL((probe_mfma_kernel<1, 1, 16, 4, 8>), grid, dim3(1024), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
+    } else if (mt == 2) {
+      grid.x = (N + 7) / 8;
+      hipExtLaunchKernelGGL((probe_mfma_kernel<2, 1, 8, 8, 8>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
+    } else if (grid.x < 256) {
+      // few column tiles: two workgroups of 32 rows each per tile
+      grid.y = (B + 31) / 32;
+      hipExtLaunchKernelGGL((probe_mfma_kernel<2, 1, 8, 8>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
+    } else if (mt == 3) {
+      hipExtLaunchKernelGGL((probe_mfma_kernel<3, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
+    } else {
+      hipExtLaunchKernelGGL((probe_mfma_kernel<4, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
     }
   }
   return hipGetLastError();

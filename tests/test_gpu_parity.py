@@ -292,7 +292,8 @@ def test_workspace_grows_across_shapes_and_streams():
 @pytest.mark.parametrize("B,d_model,dtype,Hq,d", [
     (1, 2048, "bf16", 16, 128), (17, 2560, "bf16", 16, 128), (64, 2048, "bf16", 16, 128),
     (65, 512, "bf16", 16, 128), (130, 72, "bf16", 16, 128), (3, 100, "f32", 16, 128),
-    (2048, 2048, "bf16", 16, 128), (300, 520, "bf16", 3, 64), (129, 4096, "bf16", 5, 128)])
+    (2048, 2048, "bf16", 16, 128), (300, 520, "bf16", 3, 64), (129, 4096, "bf16", 5, 128),
+    (40, 2048, "bf16", 16, 128), (48, 1024, "bf16", 32, 128), (33, 264, "bf16", 5, 64)])
 def test_probe_shapes(B, d_model, dtype, Hq, d):
     wl = WORKLOADS[2].scaled(B=B, d_model=d_model, ctx=16, dtype=dtype, Hq=Hq, Hkv=1, d=d)
     s = make_inputs(wl, 7)
