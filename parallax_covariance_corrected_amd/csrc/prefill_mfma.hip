@@ -10,9 +10,14 @@
 // Work: a workgroup owns 64 rows of one (sequence, KV head): rows are the
 // flattened (token, query head of the group) pairs, so the G query heads that
 // share a KV head share every K/V tile. Four waves of 16 rows. Keys advance in
-// blocks of 64 through double-buffered LDS (K row-major, V transposed to
-// dim-major), up to the last key any row of the workgroup may see; a wave skips
-// the blocks that lie entirely after its own rows.
+// blocks of 64 through double-buffered LDS, up to the last key any row of the
+// workgroup may see; a wave skips the blocks that lie entirely after its own
+// rows. K and V tiles go from memory straight into LDS (buffer loads with an
+// LDS destination: no staging registers, no LDS store instructions), both
+// row-major (a row per key) with their 16-byte chunks permuted per row so that
+// the operand reads below hit distinct LDS banks; the permutation is applied
+// by choosing which global chunk each lane fetches, since lane L of such a
+// load always writes the 16 bytes at the piece's base + 16 L.
 //
 // Everything is computed transposed (keys x rows), which keeps every step in
 // the lane that produced it:
@@ -28,7 +33,10 @@
 //    would cost ~1e-3 relative error), become the B operand of O^T = V^T E^T
 //    directly from the registers that hold them: the MFMA's k slots are bound
 //    to keys (4*(l/16) + t of two 16-key sub-tiles), and the A operand V^T
-//    reads the same keys from the transposed V tile.
+//    gets the same keys from the row-major V tile through the gfx950
+//    transposing LDS read (ds_read_b64_tr_b16: in each 16-lane group, lane j
+//    receives element j % 4 of the 4-element reads of lanes 4c + j / 4,
+//    c = 0..3, so a lane ends up with one dim of four keys).
 #include "common.h"
 
 namespace parallax {
@@ -41,22 +49,25 @@ constexpr float kPfRescale = 8.0f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-// K tile: row = key, D*2 bytes; 16-byte chunk c of row r at slot c ^ f(r),
-// with f chosen so that the 16 rows one operand read touches fall in distinct
-// bank groups.
+// Tiles: row = key, D*2 bytes; 16-byte chunk c of row r sits at slot
+// c ^ swz(r). K: the 16 rows one score-operand read touches (one chunk each)
+// fall in distinct bank groups. V: a transposing read touches 16 rows x 2
+// adjacent chunks (2 dt, 2 dt + 1); an even swizzle keeps the pair adjacent
+// and spreads the rows over the banks.
 template <int D>
-__device__ __forceinline__ int k_slot(int row, int chunk) {
-  if constexpr (D == 128) return row * 256 + 16 * (chunk ^ (row & 15));
-  else return row * 128 + 16 * (chunk ^ ((row >> 1) & 7));
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
-// V^T tile: row = dim, 64 keys * 2 bytes + 8 bytes of padding.
-constexpr int kVtRow = kPfKeys * 2 + 8;
+template <int D>
+__device__ __forceinline__ int v_swz(int row) { return (2 * row) & (D / 8 - 1); }
 
 template <int D>
 struct PfSmem {
   unsigned char k[2][kPfKeys * D * 2];
-  unsigned char vt[2][D * kVtRow];
+  unsigned char v[2][kPfKeys * D * 2];
 };
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ unsigned pk2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
@@ -78,13 +89,18 @@ __device__ __forceinline__ float row_sum4(float x) {
 }
 
 // CORR = false: plain softmax attention (no probe products, no e*p sums).
+// Two waves per SIMD (at most 256 registers per lane) is part of the design:
+// the second wave's MFMAs cover the first one's softmax and LDS staging. The
+// attribute keeps the register allocator from trading that occupancy away (a
+// build at one wave per SIMD measured 1.4x slower).
 template <int D, bool F32_OUT, bool CORR>
-__global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NKS = D / 32;            // 32-dim k-steps of the score product
   constexpr int NDT = D / 16;            // 16-dim output tiles
   constexpr int ROW = D * 2;             // bytes per K/V cache row
-  constexpr int CPR = D / 8;             // 16-byte chunks per cache row
-  constexpr int LOADS = kPfKeys * CPR / kPfThreads;   // 16-byte loads per thread per block
+  constexpr int PIECES = kPfKeys * ROW / 1024;        // 1 KB pieces per tile
+  static_assert(PIECES % 4 == 0, "every wave loads the same number of pieces");
   __shared__ __attribute__((aligned(16))) PfSmem<D> sm;
 
   const int lane = threadIdx.x & 63;
@@ -119,35 +135,26 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
   const __amdgpu_buffer_rsrc_t krs = make_rsrc((const uint16_t*)a.k + kv_base, (unsigned)nvalid * ROW);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const uint16_t*)a.v + kv_base, (unsigned)nvalid * ROW);
 
-  // Loads of one key block: K chunk-fastest (a row per 16 or 8 lanes, rows
-  // contiguous), V key-fastest (a wave covers 64 keys of one 8-dim chunk, so
-  // the transposed stores of a wave fill one V^T row).
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto gload = [&](int kb) {
-    const unsigned base = (unsigned)kb * kPfKeys * ROW;
+  // Key block kb -> LDS stage buf: wave w fills the 1 KB pieces w, w + 4, ...
+  // of each tile; lane L's 16 bytes land at byte 16 L of the piece, i.e. at
+  // slot (row, sc), which holds global chunk sc ^ swz(row).
+  auto stage = [&](int kb, int buf) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int idx = threadIdx.x + i * kPfThreads;
-      kreg[i] = buf_load16(krs, base + (unsigned)(idx / CPR) * ROW + 16u * (idx % CPR));
-      vreg[i] = buf_load16(vrs, base + (unsigned)(idx % kPfKeys) * ROW + 16u * (idx / kPfKeys));
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int idx = threadIdx.x + i * kPfThreads;
-      *(u32x4*)&sm.k[buf][k_slot<D>(idx / CPR, idx % CPR)] = kreg[i];
-      const int key = idx % kPfKeys, c = idx / kPfKeys;
-      unsigned char* vt = &sm.vt[buf][(8 * c) * kVtRow + 2 * key];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const unsigned w = vreg[i][e >> 1];
-        *(uint16_t*)(vt + e * kVtRow) = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
-      }
+    for (int pc = 0; pc < PIECES / 4; ++pc) {
+      const int piece = 4 * pc + wave;
+      const int byte = piece * 1024 + 16 * lane;
+      const int row = byte / ROW, sc = (byte % ROW) / 16;
+      const unsigned grow = (unsigned)(kb * kPfKeys + row) * ROW;
+      // (offsets in variables: with a device-function call inside the builtin's
+      // arguments the host compilation pass silently drops the kernel)
+      const unsigned ko = grow + 16u * (sc ^ k_swz<D>(row));
+      const unsigned vo = grow + 16u * (sc ^ v_swz<D>(row));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&sm.k[buf][piece * 1024], 16, ko, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&sm.v[buf][piece * 1024], 16, vo, 0, 0, 0);
     }
   };
 
-  gload(0);   // start streaming before the q/rho prologue
+  stage(0, 0);   // start streaming before the q/rho prologue
 
   // q and rho of this lane's row as B operands: dims 32*ks + 8*grp .. +7.
   u32x4 qb[NKS], rh[NKS], rl[NKS];
@@ -184,11 +191,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
   }
   float m_run = kNegInf, lpart = 0.f, spart = 0.f;
 
-  lstore(0);
+  // Each wave waits for its own LDS-destination loads; the barrier then
+  // publishes the whole stage.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int cur = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);
+    // stage cur ^ 1 was last read before the previous barrier
+    if (kb + 1 < nkb) stage(kb + 1, cur ^ 1);
     if (kb * kPfKeys <= wave_last_key) {
       // ---- scores and probes, 4 sub-tiles of 16 keys. k-steps outside,
       // sub-tiles inside: eight independent accumulators between dependent
@@ -201,13 +211,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
       }
       u32x4 kcur[4], knext[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kcur[j] = *(const u32x4*)&sm.k[cur][k_slot<D>(16 * j + l16, grp)];
+      for (int j = 0; j < 4; ++j)
+        kcur[j] = *(const u32x4*)&sm.k[cur][(16 * j + l16) * ROW + 16 * (grp ^ k_swz<D>(16 * j + l16))];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         if (ks + 1 < NKS) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            knext[j] = *(const u32x4*)&sm.k[cur][k_slot<D>(16 * j + l16, 4 * (ks + 1) + grp)];
+            knext[j] = *(const u32x4*)&sm.k[cur][(16 * j + l16) * ROW +
+                                                 16 * ((4 * (ks + 1) + grp) ^ k_swz<D>(16 * j + l16))];
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -279,13 +291,21 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
             pl[w] = pk2(ep[2 * w] - bf16_lo(ph[w]), ep[2 * w + 1] - bf16_hi(ph[w]));
           }
         }
-        // A operand: V^T rows 16*dt + l16, keys 32*h2 + 4*grp .. +3 and
-        // 32*h2 + 16 + 4*grp .. +3 (the keys bound to k slots t = 0..7).
-        const unsigned char* vrow = &sm.vt[cur][l16 * kVtRow + 2 * (32 * h2 + 4 * grp)];
+        // A operand: dims 16*dt + l16 of keys 32*h2 + 4*grp .. +3 and
+        // 32*h2 + 16 + 4*grp .. +3 (the keys bound to k slots t = 0..7), by two
+        // transposing reads: lane 4c + q of a 16-lane group reads dims
+        // 16*dt + 4q .. +3 of key 32*h2 + 4*grp + c (+ 16).
+        const int vkey = 32 * h2 + 4 * grp + (l16 >> 2);
+        const unsigned char* vb = &sm.v[cur][vkey * ROW + 8 * (lane & 3)];
+        const int vsw = v_swz<D>(vkey);   // the same for vkey + 16
         auto vload = [&](int dt) {
-          const u32x2 v0 = *(const u32x2*)(vrow + dt * 16 * kVtRow);
-          const u32x2 v1 = *(const u32x2*)(vrow + dt * 16 * kVtRow + 32);
-          return (u32x4){v0[0], v0[1], v1[0], v1[1]};
+          const int o = 16 * ((2 * dt) ^ vsw);
+          const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(vb + o));
+          const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(vb + 16 * ROW + o));
+          const u32x2 a0 = __builtin_bit_cast(u32x2, r0), a1 = __builtin_bit_cast(u32x2, r1);
+          return (u32x4){a0[0], a0[1], a1[0], a1[1]};
         };
         // hi terms of tile dt, then lo terms of tile dt - 1: no accumulator is
         // hit by two MFMAs in a row.
@@ -310,7 +330,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_mfma_kernel(PrefillArgs a)
           op[NDT - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vprev), as_bf16x8(pl), op[NDT - 1], 0, 0, 0);
       }
     }
-    if (kb + 1 < nkb) lstore(cur ^ 1);   // that stage was last read before the barrier
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
