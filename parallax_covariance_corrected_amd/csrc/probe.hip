@@ -64,6 +64,10 @@ __global__ __launch_bounds__(NW * 64) void probe_mfma_kernel(const uint16_t* __r
         wb[u][jn] = buf_load16(wr, 16 * jn + l16 < COLS ? (unsigned)(16 * jn + l16) * rowb + koff
                                                         : 0x80000000u);
     }
+    // Keep every load above in flight together: left alone, the scheduler
+    // interleaves them with the MFMAs below to save registers, and the wave
+    // then waits out several memory round trips per U steps instead of one.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
