@@ -15,12 +15,15 @@
 // read zeros (buffer range). Larger batches (B > 64): an LDS-tiled GEMM with
 // 128 x 128 tiles (below), where operand reuse across waves pays for staging.
 // fp32 kernel: one thread per output, a plain dot product.
+#include <type_traits>
+
 #include "common.h"
 
 namespace parallax {
 namespace {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+typedef __attribute__((address_space(3))) void lds_void;
 
 // COLS < 16 (with NT = 1): the workgroup owns only COLS output columns (the
 // other MFMA columns read zeros), so twice as many workgroups share the W_R
@@ -109,31 +112,39 @@ __global__ __launch_bounds__(NW * 64) void probe_mfma_kernel(const uint16_t* __r
 
 // Large-batch probe: a 128 x 128 tile of rho per workgroup, eight waves in a
 // 4 x 2 arrangement each owning 32 x 64 (2 x 4 MFMA tiles). K advances in
-// steps of 64 through double-buffered LDS, so every workgroup reads its x and
-// W_R panels from the caches once. LDS rows are 128 bytes (eight 16-byte
-// chunks); chunk c of row r sits at slot c ^ ((r >> 1) & 7). With that swizzle
-// the 16 rows one MFMA operand read touches, and the two rows a quarter-wave
-// stores, fall in distinct bank groups (no conflicts, no padding).
-constexpr int kGM = 128, kGN = 128, kGK = 64;
+// steps of 128 through double-buffered LDS (2 x 64 KB), so every workgroup
+// reads its x and W_R panels from the caches once. The panels go from memory
+// straight into LDS (buffer loads with an LDS destination: lane L of a load
+// writes the 16 bytes at the piece's base + 16 L), so no registers hold them
+// in transit and no LDS store instructions are issued. LDS rows are 256 bytes
+// (sixteen 16-byte chunks); chunk c of row r sits at slot c ^ (r & 15), chosen
+// by the global chunk each lane fetches, which puts the 16 rows of one MFMA
+// operand read in distinct bank groups. The four LDS buffers are separate
+// arrays and each loop half names its own: with one array indexed by a
+// run-time stage, the compiler could not tell that the operand reads of one
+// stage never touch the stage being loaded and waited for the loads first.
+constexpr int kGM = 128, kGN = 128, kGK = 128;
 constexpr int kGWM = 4, kGWN = 2;                  // wave grid
 constexpr int kGTI = kGM / 16 / kGWM;              // MFMA tiles per wave, rows
 constexpr int kGTJ = kGN / 16 / kGWN;              // MFMA tiles per wave, columns
-constexpr int kGThreads = 64 * kGWM * kGWN;
-constexpr int kRowChunks = kGK / 8;                // 16-byte chunks per LDS row
-constexpr int kLdsRow = kGK * 2;
-constexpr int kLoadsA = kGM * kRowChunks / kGThreads, kLoadsB = kGN * kRowChunks / kGThreads;
+constexpr int kGWaves = kGWM * kGWN;
+constexpr int kGThreads = 64 * kGWaves;
+constexpr int kLdsRow = kGK * 2;                   // bytes per LDS row (16 chunks)
+constexpr int kPieces = kGM * kLdsRow / 1024;      // 1 KB pieces per operand panel
+static_assert(kGM == kGN && kPieces % kGWaves == 0, "every wave loads the same pieces");
 
 __device__ __forceinline__ int lds_slot(int row, int chunk) {
-  return row * kLdsRow + 16 * (chunk ^ ((row >> 1) & (kRowChunks - 1)));
+  return row * kLdsRow + 16 * (chunk ^ (row & 15));
 }
 
 __global__ __launch_bounds__(kGThreads) void probe_gemm_kernel(const uint16_t* __restrict__ W,
                                                                const uint16_t* __restrict__ x,
                                                                float* __restrict__ rho, int B,
                                                                int N, int K) {
-  __shared__ __attribute__((aligned(16))) unsigned char sA[2][kGM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) unsigned char sB[2][kGN * kLdsRow];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(16))) unsigned char sA0[kGM * kLdsRow], sA1[kGM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) unsigned char sB0[kGN * kLdsRow], sB1[kGN * kLdsRow];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
   const int wm = wave / kGWN, wn = wave % kGWN;
   const int m0 = blockIdx.y * kGM, n0 = blockIdx.x * kGN;
@@ -141,31 +152,20 @@ __global__ __launch_bounds__(kGThreads) void probe_gemm_kernel(const uint16_t* _
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (size_t)m0 * K, (unsigned)min(B - m0, kGM) * rowb);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + (size_t)n0 * K, (unsigned)min(N - n0, kGN) * rowb);
 
-  // Global -> registers -> LDS: load c of thread t moves chunk (t + c*threads)
-  // of the tile, row-major (consecutive threads read consecutive 16 bytes).
-  u32x4 ga[kLoadsA], gb[kLoadsB];
-  auto gload = [&](int k0) {
+  // Panels of k0 .. k0 + kGK - 1 -> stage BUF: wave w loads pieces w, w + 8, ...
+  // of each panel. Rows past B (or N) and columns past K read as zero.
+  auto stage = [&](int k0, auto BUF) {
+    unsigned char* a = decltype(BUF)::value ? sA1 : sA0;
+    unsigned char* b = decltype(BUF)::value ? sB1 : sB0;
 #pragma unroll
-    for (int c = 0; c < kLoadsA; ++c) {
-      const int idx = tid + c * kGThreads, kk = k0 + 8 * (idx % kRowChunks);
-      ga[c] = buf_load16(xr, kk < K ? (unsigned)(idx / kRowChunks) * rowb + (unsigned)kk * 2 : 0x80000000u);
-    }
-#pragma unroll
-    for (int c = 0; c < kLoadsB; ++c) {
-      const int idx = tid + c * kGThreads, kk = k0 + 8 * (idx % kRowChunks);
-      gb[c] = buf_load16(wr, kk < K ? (unsigned)(idx / kRowChunks) * rowb + (unsigned)kk * 2 : 0x80000000u);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < kLoadsA; ++c) {
-      const int idx = tid + c * kGThreads;
-      *(u32x4*)&sA[buf][lds_slot(idx / kRowChunks, idx % kRowChunks)] = ga[c];
-    }
-#pragma unroll
-    for (int c = 0; c < kLoadsB; ++c) {
-      const int idx = tid + c * kGThreads;
-      *(u32x4*)&sB[buf][lds_slot(idx / kRowChunks, idx % kRowChunks)] = gb[c];
+    for (int pc = 0; pc < kPieces / kGWaves; ++pc) {
+      const int piece = pc * kGWaves + wave;
+      const int byte = piece * 1024 + 16 * lane;
+      const int row = byte / kLdsRow, sc = (byte % kLdsRow) / 16;
+      const int kk = k0 + 8 * (sc ^ (row & 15));
+      const unsigned off = kk < K ? (unsigned)row * rowb + (unsigned)kk * 2 : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)&a[piece * 1024], 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)&b[piece * 1024], 16, off, 0, 0, 0);
     }
   };
 
@@ -176,21 +176,22 @@ __global__ __launch_bounds__(kGThreads) void probe_gemm_kernel(const uint16_t* _
     for (int jn = 0; jn < kGTJ; ++jn) acc[i][jn] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   const int nk = (K + kGK - 1) / kGK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kGK);   // next panels in flight
+  // One K step on stage CUR while the next one loads into the other stage
+  // (last read before the previous barrier).
+  auto step = [&](int kt, auto CUR) {
+    constexpr int cur = decltype(CUR)::value;
+    const unsigned char* a = cur ? sA1 : sA0;
+    const unsigned char* b = cur ? sB1 : sB0;
+    if (kt + 1 < nk) stage((kt + 1) * kGK, std::integral_constant<int, cur ^ 1>{});
 #pragma unroll
     for (int ks = 0; ks < kGK / 32; ++ks) {
       u32x4 av[kGTI], bv[kGTJ];
 #pragma unroll
       for (int i = 0; i < kGTI; ++i)
-        av[i] = *(const u32x4*)&sA[cur][lds_slot(wm * 16 * kGTI + 16 * i + l16, 4 * ks + grp)];
+        av[i] = *(const u32x4*)&a[lds_slot(wm * 16 * kGTI + 16 * i + l16, 4 * ks + grp)];
 #pragma unroll
       for (int jn = 0; jn < kGTJ; ++jn)
-        bv[jn] = *(const u32x4*)&sB[cur][lds_slot(wn * 16 * kGTJ + 16 * jn + l16, 4 * ks + grp)];
+        bv[jn] = *(const u32x4*)&b[lds_slot(wn * 16 * kGTJ + 16 * jn + l16, 4 * ks + grp)];
 #pragma unroll
       for (int i = 0; i < kGTI; ++i)
 #pragma unroll
@@ -198,8 +199,17 @@ __global__ __launch_bounds__(kGThreads) void probe_gemm_kernel(const uint16_t* _
           acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(bv[jn]),
                                                                 acc[i][jn], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);   // the other buffer was last read before the barrier
+    // each wave waits for its own LDS-destination loads; the barrier then
+    // publishes the whole stage
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  stage(0, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
   }
 
 #pragma unroll
