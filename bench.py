@@ -299,7 +299,9 @@ def run_workload(args, wl_id: int, emit: bool = True):
 def run_sweep(args):
     """Batch x context sweep at Hq=16, Hkv=8, d=128 bf16 (decode split-K pass +
     merge, rotated K/V sets so that every rep reads cold data); one JSON line
-    per point. GB/s counts K/V, q, rho, out and seq_lens."""
+    per point. GB/s counts K/V, q, rho, out and seq_lens; `pct_peak` is over
+    the whole call (both launches), `kernel_pct_peak` over the decode kernel's
+    own duration (per-launch events)."""
     import torch
     from parallax_covariance_corrected_amd import binding as pb
     from parallax_covariance_corrected_amd.workloads import sweep_points
@@ -332,13 +334,24 @@ def run_sweep(args):
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
+        # the same calls again with per-launch events: the decode kernel alone
+        pb.profile_reset()
+        with pb.options(profile=1):
+            for i in range(reps):
+                K, V = sets[i % nsets]
+                pb.decode(q, rho, K, V, lens, out=out)
+            torch.cuda.synchronize()
+            kms, kn = pb.profile_read(pb.KERNEL_DECODE)
+        kus = kms / kn * 1e3
         byts = kv + B * 16 * 128 * (2 + 4 + 2) + B * 4
         chunk, splits, kern = pb.decode_plan(B, 16, 8, 128, ctx)
         print(json.dumps({"sweep": True, "B": B, "ctx": ctx, "plan": [chunk, splits, kern],
                           "us_per_step": round(us, 2),
                           "tokens_per_s": round(B / (us * 1e-6), 1),
                           "gbps": round(byts / (us * 1e-6) / 1e9, 1),
-                          "pct_peak": round(100 * byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)}),
+                          "pct_peak": round(100 * byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+                          "kernel_us": round(kus, 2),
+                          "kernel_pct_peak": round(100 * byts / (kus * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)}),
               flush=True)
         del sets, q, rho, lens, out
         torch.cuda.empty_cache()
