@@ -121,11 +121,12 @@ int get_workspace(hipStream_t stream, size_t bytes, void** base) {
     nw.bytes = round_up(std::max(bytes, w.bytes), 1 << 20);
     e = hipMallocAsync(&nw.base, nw.bytes, stream);
     if (e != hipSuccess || !nw.base) return fail(PARALLAX_ERR_NO_MEMORY, "workspace allocation failed");
-    if (w.base) {
-      e = hipFreeAsync(w.base, stream);
+    void* old = w.base;
+    w = nw;   // the new buffer is in use from here on, whatever happens to the old one
+    if (old) {
+      e = hipFreeAsync(old, stream);
       if (e != hipSuccess) return hip_fail(e, "hipFreeAsync");
     }
-    w = nw;
   }
   *base = w.base;
   return PARALLAX_OK;

@@ -176,13 +176,15 @@ def test_split_and_kernel_invariance(chunk, kernel, items):
     assert rel_l2(o32, ref) <= 1e-5 and max_abs(o32, ref) <= 1e-4
 
 
-@pytest.mark.parametrize("B", [70, 130])
+@pytest.mark.parametrize("B", [70, 130, 256, 257])
 def test_compacted_item_order_matches_split_major(B):
     """Numbering only the non-empty work items (a ragged batch in a cache of
-    many chunks; sequences in two or three groups of 64) computes the same
+    many chunks; sequences in two to four groups of 64) computes the same
     items as the split-major numbering of every item: equal bit for bit, and
     right against the oracle when the workspace still holds another input's
-    partial states (an item left out would leave one of those behind)."""
+    partial states (an item left out would leave one of those behind). At
+    B = 257 the compacted numbering does not apply and the option falls back
+    to split-major."""
     wl = WORKLOADS[5].scaled(B=B, Hq=8, Hkv=2, ctx=2000, d_model=256)
     r = np.random.default_rng(B)
     lens = [0, 1, 255, 256, 257, 2000] + [int(x) for x in r.integers(0, 2001, B - 6)]
