@@ -250,7 +250,7 @@ def run_workload(args, wl_id: int, emit: bool = True):
     dec_bytes = sum(a["decode_read"] for a in ab) / len(ab)
     dec_avg_ms = dec_ms / max(dec_n, 1)
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name) if wl_id == 2 else None
+    traffic = measured_traffic(wl.name)
     rec = {
         "metric": METRIC,
         "value": round(wl.B / (ms_step * 1e-3), 1),
