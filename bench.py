@@ -12,7 +12,8 @@ Output: one JSON line (metric, value = decode tokens/s, ms_per_step, roofline
 of the dominant kernel, CPU oracle baseline, ...).
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload 2]
-                    [--sets 3] [--no-cpu-baseline] [--sweep] [--copy-calibration]
+                    [--sets 3] [--no-cpu-baseline] [--sweep] [--fusion-sweep]
+                    [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -69,8 +70,46 @@ def upload_set(s, device="cuda"):
 
 
 def step(pb, wl, d):
+    """One decode step: probe and decode in one library call (the plan places
+    the probe inside the decode kernel or in a launch of its own)."""
+    pb.probe_decode(d["W_R"], d["x"], d["q"], d["K"], d["V"], d["seq_lens"], out=d["out"])
+
+
+def fill_rho(pb, wl, d):
+    """rho of a set in its own buffer, for the decode-only measurements."""
     pb.probe(d["W_R"], d["x"], wl.Hq, wl.d, out=d["rho"])
-    pb.decode(d["q"], d["rho"], d["K"], d["V"], d["seq_lens"], out=d["out"])
+
+
+def timed_steps(fn, reps: int, warm: int = 5) -> float:
+    """Average microseconds of fn(i) over reps calls, events on the current stream."""
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def probe_fusion(pb, wl, dev_sets, reps: int):
+    """Whole-step time with the probe in a launch of its own and inside the
+    decode kernel (where the plan can place it there), same inputs."""
+    code = pb.BF16 if wl.dtype == "bf16" else pb.F32
+    auto = pb.probe_decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.d_model, wl.capacity, code)
+    rec = {"auto_plan": "fused" if auto else "separate"}
+    for name, f in (("separate", 1), ("fused", 2)):
+        with pb.options(fuse=f):
+            if f == 2 and not pb.probe_decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.d_model,
+                                                   wl.capacity, code):
+                rec[f"{name}_step_us"] = None
+                continue
+            rec[f"{name}_step_us"] = round(
+                timed_steps(lambda i: step(pb, wl, dev_sets[i % len(dev_sets)]), reps), 3)
+    return rec
 
 
 def cpu_baseline(s, budget_s: float = 12.0):
@@ -117,16 +156,7 @@ def matched_ratios(pb, wl, dev_sets, reps: int):
     out2 = torch.empty_like(q2[0])
 
     def timed(fn):
-        for i in range(5):
-            fn(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(reps):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
+        return timed_steps(fn, reps)
 
     def par(i):
         d = dev_sets[i % len(dev_sets)]
@@ -210,10 +240,13 @@ def run_workload(args, wl_id: int, emit: bool = True):
     print(f"# bench: generating {args.sets} input sets for {wl.name}", file=sys.stderr, flush=True)
     sets_host = [make_inputs(wl, seed) for seed in range(args.sets)]
     dev_sets = [upload_set(s) for s in sets_host]
+    for d in dev_sets:
+        fill_rho(pb, wl, d)
     torch.cuda.synchronize()
     tokens = [s.total_tokens() for s in sets_host]
-    chunk, splits, kernel = pb.decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.capacity,
-                                           pb.BF16 if wl.dtype == "bf16" else pb.F32)
+    code = pb.BF16 if wl.dtype == "bf16" else pb.F32
+    chunk, splits, kernel = pb.decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.capacity, code)
+    fused = pb.probe_decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.d_model, wl.capacity, code)
 
     for i in range(args.warmup):
         step(pb, wl, dev_sets[i % len(dev_sets)])
@@ -267,13 +300,15 @@ def run_workload(args, wl_id: int, emit: bool = True):
         "config": {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d,
                    "ctx": wl.ctx, "max_ctx": wl.capacity, "d_model": wl.d_model,
                    "kv_dtype": wl.dtype, "input_sets_rotated": args.sets,
-                   "plan": {"chunk": chunk, "splits": splits, "kernel": kernel}},
+                   "plan": {"chunk": chunk, "splits": splits, "kernel": kernel,
+                            "probe": "fused" if fused else "separate"}},
         "hbm_gbps_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "pct_peak_step": round(100 * step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_mfma_kernel (split-K pass)",
+                     "kernel": ("decode_mfma_kernel" if kernel >= 2 else "decode_generic_kernel")
+                               + (" (probe fused in)" if fused else " (split-K pass)"),
                      "bytes_per_launch": int(dec_bytes),
                      "avg_launch_us": round(dec_avg_ms * 1e3, 3),
                      "merge_avg_us": round(mrg_ms / max(mrg_n, 1) * 1e3, 3),
@@ -281,9 +316,9 @@ def run_workload(args, wl_id: int, emit: bool = True):
         "cpu_baseline": None,
     }
     rec["step_time_distribution"] = step_percentiles(pb, wl, dev_sets, args.steps)
+    rec["probe_fusion"] = probe_fusion(pb, wl, dev_sets, min(args.steps, 100))
     if wl.dtype == "bf16":
         rec["matched"] = matched_ratios(pb, wl, dev_sets, args.steps)
-        step(pb, wl, dev_sets[0])
         rec["correction_to_output"] = correction_ratio(pb, dev_sets[0])
         ceiling = read_ceiling(pb)
         rec["roofline"]["read_ceiling_gbps"] = round(ceiling, 1)
@@ -355,6 +390,51 @@ def run_sweep(args):
               flush=True)
         del sets, q, rho, lens, out
         torch.cuda.empty_cache()
+
+
+def run_fusion_sweep(args):
+    """Whole-step time of parallax_probe_decode with the probe in its own launch
+    and inside the decode kernel, over batch x d_model x context (bf16, Hq=16,
+    Hkv=8, d=128; and the fp32 tiny shape family), three rotated input sets
+    drawn on the device. One line per point on stdout (markdown table)."""
+    import torch
+    from parallax_covariance_corrected_amd import binding as pb
+    g = torch.Generator(device="cuda").manual_seed(0)
+    pts = [("bf16", B, 16, 8, 128, dm, ctx) for B in (1, 4, 16, 64)
+           for dm in (64, 128, 256, 512, 1024, 2048) for ctx in (128, 1024, 4096)]
+    pts += [("f32", B, 2, 2, 64, dm, ctx) for B in (1, 4) for dm in (128, 512) for ctx in (128, 1024)]
+    print("| dtype | B | Hq/Hkv | d | d_model | ctx | plan kernel, splits | W_R bytes per item "
+          "| items | separate us | fused us | fused/separate | auto |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for (dt, B, Hq, Hkv, d, dm, ctx) in pts:
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        code = pb.BF16 if dt == "bf16" else pb.F32
+
+        def rnd(*shape, std=1.0):
+            return (torch.randn(*shape, generator=g, device="cuda") * std).to(tdt)
+        sets = [dict(W_R=rnd(Hq * d, dm, std=0.02), x=rnd(B, dm), q=rnd(B, Hq, d),
+                     K=rnd(B, Hkv, ctx, d), V=rnd(B, Hkv, ctx, d),
+                     seq_lens=torch.full((B,), ctx, dtype=torch.int32, device="cuda"),
+                     out=torch.empty((B, Hq, d), dtype=tdt, device="cuda")) for _ in range(3)]
+
+        def run(i):
+            e = sets[i % 3]
+            pb.probe_decode(e["W_R"], e["x"], e["q"], e["K"], e["V"], e["seq_lens"], out=e["out"])
+        _, splits, kern = pb.decode_plan(B, Hq, Hkv, d, ctx, code)
+        G = Hq // Hkv
+        gh = G if G <= 4 else 4
+        item = gh * d * dm * (2 if dt == "bf16" else 4)
+        items = B * Hkv * (G // gh) * splits
+        with pb.options(fuse=1):
+            t_sep = timed_steps(run, args.steps)
+        with pb.options(fuse=2):
+            can = pb.probe_decode_plan(B, Hq, Hkv, d, dm, ctx, code)
+            t_fus = timed_steps(run, args.steps) if can else float("nan")
+        auto = pb.probe_decode_plan(B, Hq, Hkv, d, dm, ctx, code)
+        print(f"| {dt} | {B} | {Hq}/{Hkv} | {d} | {dm} | {ctx} | {kern}, {splits} | {item} | {items} "
+              f"| {t_sep:.2f} | {t_fus:.2f} | {t_fus / t_sep:.3f} | {'fused' if auto else 'separate'} |",
+              flush=True)
+        del sets
 
 
 def run_prefill(args):
@@ -477,6 +557,9 @@ def main():
                     help="first copy 256 MiB device-to-device 3 times (a kernel of known "
                          "traffic, to scale hardware byte counters)")
     ap.add_argument("--sweep-max-gib", type=int, default=0)
+    ap.add_argument("--fusion-sweep", action="store_true",
+                    help="time the probe inside the decode kernel against a separate probe "
+                         "launch over batch x d_model x context")
     ap.add_argument("--prefill", action="store_true",
                     help="measure the causal many-query forward instead of decode")
     ap.add_argument("--prefill-T", type=int, default=4096)
@@ -502,6 +585,9 @@ def main():
         del src, dst
     if args.sweep:
         run_sweep(args)
+        return
+    if args.fusion_sweep:
+        run_fusion_sweep(args)
         return
     if args.prefill:
         run_prefill(args)

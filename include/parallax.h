@@ -123,6 +123,45 @@ int parallax_softmax_decode(const void* q, const void* k_cache, const void* v_ca
                             int max_ctx, int dtype, hipStream_t stream);
 
 /*
+ * parallax_probe_decode — one whole decode step: the probe rho = W_R x of every
+ * query head and the Parallax decode that uses it, in one call. The probe is
+ * computed from the layer input as part of the attention step (zubnet.ai (pt),
+ * "Parallax mantém softmax ...", second paragraph: the probe comes from the
+ * layer input through the learned W_R, and the correction reuses the KV stream
+ * of softmax attention).
+ *
+ *   W_R, x   : as parallax_probe (W_R [Hq*d, d_model], x [B, d_model])
+ *   q, k_cache, v_cache, seq_lens, out : as parallax_decode
+ *
+ * The result equals parallax_probe followed by parallax_decode on the same
+ * inputs, up to fp32 rounding of rho. Two plans (parallax_probe_decode_plan
+ * tells which one a shape gets):
+ *   - fused: the decode kernel computes rho of each work item's query heads
+ *     from W_R and x in its prologue, into on-chip memory; rho is never
+ *     written to device memory and the step is one launch (plus the merge of
+ *     split sequences). Each work item then reads G*d rows of W_R, so this is
+ *     chosen only where those reads are small per item and in total (small
+ *     d_model and few work items): there they cost less than a launch.
+ *   - separate: the probe kernel writes rho into the library's workspace (the
+ *     same per-stream workspace as the split states, grown the same way), then
+ *     the decode runs as parallax_decode.
+ * Requires the argument rules of both parallax_probe and parallax_decode;
+ * errors as theirs. Enqueue-only on `stream`.
+ */
+int parallax_probe_decode(const void* W_R, const void* x, const void* q, const void* k_cache,
+                          const void* v_cache, const int* seq_lens, void* out,
+                          int B, int Hq, int Hkv, int d, int d_model, int max_ctx, int dtype,
+                          hipStream_t stream);
+
+/*
+ * parallax_probe_decode_plan — writes 1 to *fused when parallax_probe_decode
+ * would compute the probe inside the decode kernel for this shape, else 0.
+ * Same shape checks as parallax_decode; d_model >= 1.
+ */
+int parallax_probe_decode_plan(int B, int Hq, int Hkv, int d, int d_model, int max_ctx, int dtype,
+                               int* fused);
+
+/*
  * parallax_prefill — the causal many-query forward (prefill or chunked
  * prefill): T new tokens per sequence, each attending to the cache up to and
  * including its own position. The layer is pretrained as language-model
@@ -191,13 +230,20 @@ int parallax_decode_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
  *                          1 = every (split, sequence, head) item, split-major,
  *                          2 = only the non-empty ones (up to 256 sequences and
  *                          64 splits; otherwise as 1)
+ *   PARALLAX_OPT_FUSE    : probe placement in parallax_probe_decode:
+ *                          0 = automatic, 1 = always a separate probe launch,
+ *                          2 = inside the decode kernel wherever its plan
+ *                          allows it (generic kernel, or four-wave items
+ *                          without the compacted numbering; d_model * element
+ *                          size a multiple of 16 bytes)
  */
 typedef enum {
   PARALLAX_OPT_CHUNK = 1,
   PARALLAX_OPT_KERNEL = 2,
   PARALLAX_OPT_PROFILE = 3,
   PARALLAX_OPT_ITEMS = 4,
-  PARALLAX_OPT_ORDER = 5
+  PARALLAX_OPT_ORDER = 5,
+  PARALLAX_OPT_FUSE = 6
 } parallax_option;
 
 int parallax_set_option(int option, int value);

@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_MEMORY = 0, 1, 2, 3, 4
 F32, BF16, BF16_F32OUT = 0, 1, 2
-OPT_CHUNK, OPT_KERNEL, OPT_PROFILE, OPT_ITEMS, OPT_ORDER = 1, 2, 3, 4, 5
+OPT_CHUNK, OPT_KERNEL, OPT_PROFILE, OPT_ITEMS, OPT_ORDER, OPT_FUSE = 1, 2, 3, 4, 5, 6
 KERNEL_PROBE, KERNEL_DECODE, KERNEL_MERGE, KERNEL_PREFILL, KERNEL_READ = 0, 1, 2, 3, 4
 
 _lib = None
@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
         L.parallax_read_bandwidth.argtypes = [vp, ctypes.c_longlong, vp, vp]
         L.parallax_decode_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i),
                                            ctypes.POINTER(i), ctypes.POINTER(i)]
+        L.parallax_probe_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+        L.parallax_probe_decode_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i)]
         L.parallax_set_option.argtypes = [i, i]
         L.parallax_get_option.argtypes = [i, ctypes.POINTER(i)]
         L.parallax_profile_read.argtypes = [i, ctypes.POINTER(ctypes.c_double),
@@ -55,7 +57,7 @@ def lib() -> ctypes.CDLL:
         L.parallax_profile_reset.argtypes = []
         for name in ("parallax_probe", "parallax_decode", "parallax_softmax_decode",
                      "parallax_prefill", "parallax_softmax_prefill", "parallax_read_bandwidth",
-                     "parallax_decode_plan",
+                     "parallax_decode_plan", "parallax_probe_decode", "parallax_probe_decode_plan",
                      "parallax_set_option", "parallax_get_option", "parallax_profile_read",
                      "parallax_profile_reset"):
             getattr(L, name).restype = i
@@ -140,6 +142,36 @@ def decode(q: torch.Tensor, rho: torch.Tensor, k_cache: torch.Tensor, v_cache: t
     return out
 
 
+def probe_decode(W_R: torch.Tensor, x: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                 v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                 out: Optional[torch.Tensor] = None,
+                 out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """One whole decode step (probe rho = W_R x, then the Parallax decode):
+    out[B, Hq, d] from W_R[Hq*d, d_model], x[B, d_model], q[B, Hq, d],
+    k_cache/v_cache[B, Hkv, max_ctx, d] and seq_lens[B] (int32), on the
+    current stream."""
+    for t, nm in ((W_R, "W_R"), (x, "x"), (q, "q"), (k_cache, "k_cache"),
+                  (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _need(t, nm)
+    B, Hq, d = q.shape
+    _, Hkv, max_ctx, _ = k_cache.shape
+    d_model = x.shape[1]
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    if any(t.dtype != q.dtype for t in (W_R, x, k_cache, v_cache)):
+        raise ValueError("W_R, x, q, k_cache and v_cache must share a dtype")
+    if tuple(W_R.shape) != (Hq * d, d_model) or x.shape[0] != B:
+        raise ValueError("W_R must be [Hq*d, d_model] and x [B, d_model]")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out")
+    code = _dtype_code(q.dtype, out.dtype)
+    _check(lib().parallax_probe_decode(_ptr(W_R), _ptr(x), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(seq_lens), _ptr(out), B, Hq, Hkv, d, d_model, max_ctx,
+                                       code, _stream()))
+    return out
+
+
 def softmax_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    seq_lens: torch.Tensor, out: Optional[torch.Tensor] = None,
                    out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
@@ -217,6 +249,15 @@ def decode_plan(B: int, Hq: int, Hkv: int, d: int, max_ctx: int, dtype: int = BF
     return c.value, s.value, k.value
 
 
+def probe_decode_plan(B: int, Hq: int, Hkv: int, d: int, d_model: int, max_ctx: int,
+                      dtype: int = BF16) -> bool:
+    """Whether probe_decode computes the probe inside the decode kernel for this shape."""
+    f = ctypes.c_int()
+    _check(lib().parallax_probe_decode_plan(B, Hq, Hkv, d, d_model, max_ctx, dtype,
+                                            ctypes.byref(f)))
+    return bool(f.value)
+
+
 def set_option(option: int, value: int):
     _check(lib().parallax_set_option(option, value))
 
@@ -243,7 +284,7 @@ class options:
 
     def __init__(self, **kw):
         self.kw = {{"chunk": OPT_CHUNK, "kernel": OPT_KERNEL, "profile": OPT_PROFILE,
-                    "items": OPT_ITEMS, "order": OPT_ORDER}[k]: v
+                    "items": OPT_ITEMS, "order": OPT_ORDER, "fuse": OPT_FUSE}[k]: v
                    for k, v in kw.items()}
         self.saved = {}
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <iterator>
 #include <map>
 #include <mutex>
 #include <string>
@@ -39,6 +40,7 @@ int g_opt_kernel = 0;
 int g_opt_profile = 0;
 int g_opt_items = 0;
 int g_opt_order = 0;
+int g_opt_fuse = 0;
 
 // ---------------------------------------------------------------- profiling
 // Start/stop events are handed to hipExtLaunchKernel, which stamps them from
@@ -140,6 +142,24 @@ struct Plan {
   int compact;  // 1: compacted item numbering (kernel 2 only)
 };
 
+// Probe fused into the decode prologue (parallax_probe_decode): every work item
+// recomputes rho of its head block from W_R (GH*d rows of d_model elements), so
+// W_R is read once per work item instead of once per call — from the caches
+// after the first time, but still through each compute unit. That replaces the
+// probe launch (a few microseconds whatever its size) only where the reads per
+// item and in total stay small. Limits from timing whole steps both ways over
+// batch 1-64 x d_model 64-2048 x context 128-4096 (Hq 16, Hkv 8, d 128, bf16;
+// and fp32 shapes): on the matrix-core kernel fusing was 3-28% faster at
+// 32 KiB per item and 2-12% at 64 KiB per item with up to 8 MiB in all, and
+// slower beyond (up to 2.4x at 1 MiB per item); on the generic kernel, whose
+// decode is slower and hides more of the prologue, 13-25% faster up to
+// 128 KiB per item.
+struct FuseLimit {
+  long long item_bytes, total_bytes;
+};
+constexpr FuseLimit kFuseMfma[] = {{32LL << 10, 16LL << 20}, {64LL << 10, 8LL << 20}};
+constexpr FuseLimit kFuseGeneric[] = {{128LL << 10, 8LL << 20}};
+
 int esize(int dtype) { return dtype == PARALLAX_F32 ? 4 : 2; }
 
 int check_decode_shape(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
@@ -214,6 +234,41 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
   return p;
 }
 
+// Whether parallax_probe_decode runs the probe inside the decode kernel for
+// this plan (shapes already checked).
+bool fuse_probe(const Plan& p, int B, int Hq, int Hkv, int d, int d_model, int dtype) {
+  const int es = esize(dtype);
+  const bool can = (p.kernel == 1 || (p.kernel == 2 && !p.compact)) && (d_model * es) % 16 == 0;
+  if (!can || g_opt_fuse == 1) return false;
+  if (g_opt_fuse == 2) return true;
+  const int G = Hq / Hkv;
+  const int GH = head_block(G, p.kernel >= 2);
+  const long long item_bytes = (long long)GH * d * d_model * es;
+  const long long total = (long long)B * Hkv * (G / GH) * p.splits * item_bytes;
+  auto within = [&](const FuseLimit& f) {
+    return item_bytes <= f.item_bytes && total <= f.total_bytes;
+  };
+  if (p.kernel >= 2) return std::any_of(std::begin(kFuseMfma), std::end(kFuseMfma), within);
+  return std::any_of(std::begin(kFuseGeneric), std::end(kFuseGeneric), within);
+}
+
+int check_probe(const void* W_R, const void* x, int B, int Hq, int d, int d_model, int dtype) {
+  if (dtype != PARALLAX_F32 && dtype != PARALLAX_BF16 && dtype != PARALLAX_BF16_F32OUT)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
+  if (!W_R || !x) return fail(PARALLAX_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(W_R, 16) || !aligned(x, 16))
+    return fail(PARALLAX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (B < 1 || Hq < 1 || d_model < 1)
+    return fail(PARALLAX_ERR_INVALID_ARG, "B, Hq and d_model must be >= 1");
+  if (d != 64 && d != 128) return fail(PARALLAX_ERR_UNSUPPORTED, "head dim d must be 64 or 128");
+  if (dtype != PARALLAX_F32 && d_model % 8 != 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "d_model must be a multiple of 8 for bf16");
+  if ((long long)d_model * 2 * 64 >= (1LL << 30) || (long long)Hq * d > (1LL << 28) ||
+      (long long)B > (1LL << 22))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "probe size out of range");
+  return PARALLAX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,6 +298,10 @@ int parallax_set_option(int option, int value) {
       if (value < 0 || value > 2) return fail(PARALLAX_ERR_INVALID_ARG, "order must be 0, 1 or 2");
       g_opt_order = value;
       return PARALLAX_OK;
+    case PARALLAX_OPT_FUSE:
+      if (value < 0 || value > 2) return fail(PARALLAX_ERR_INVALID_ARG, "fuse must be 0, 1 or 2");
+      g_opt_fuse = value;
+      return PARALLAX_OK;
 
     default:
       return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
@@ -257,6 +316,7 @@ int parallax_get_option(int option, int* value) {
     case PARALLAX_OPT_PROFILE: *value = g_opt_profile; return PARALLAX_OK;
     case PARALLAX_OPT_ITEMS: *value = g_opt_items; return PARALLAX_OK;
     case PARALLAX_OPT_ORDER: *value = g_opt_order; return PARALLAX_OK;
+    case PARALLAX_OPT_FUSE: *value = g_opt_fuse; return PARALLAX_OK;
     default: return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
   }
 }
@@ -300,22 +360,13 @@ int parallax_profile_read(int kernel, double* total_ms, long long* launches) {
 
 int parallax_probe(const void* W_R, const void* x, float* rho, int B, int Hq, int d,
                    int d_model, int dtype, hipStream_t stream) {
-  if (dtype != PARALLAX_F32 && dtype != PARALLAX_BF16 && dtype != PARALLAX_BF16_F32OUT)
-    return fail(PARALLAX_ERR_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
-  if (!W_R || !x || !rho) return fail(PARALLAX_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned(W_R, 16) || !aligned(x, 16) || !aligned(rho, 16))
-    return fail(PARALLAX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
-  if (B < 1 || Hq < 1 || d_model < 1)
-    return fail(PARALLAX_ERR_INVALID_ARG, "B, Hq and d_model must be >= 1");
-  if (d != 64 && d != 128) return fail(PARALLAX_ERR_UNSUPPORTED, "head dim d must be 64 or 128");
-  const bool f32 = dtype == PARALLAX_F32;
-  if (!f32 && d_model % 8 != 0)
-    return fail(PARALLAX_ERR_INVALID_ARG, "d_model must be a multiple of 8 for bf16");
-  if ((long long)d_model * 2 * 64 >= (1LL << 30) || (long long)Hq * d > (1LL << 28) ||
-      (long long)B > (1LL << 22))
-    return fail(PARALLAX_ERR_UNSUPPORTED, "probe size out of range");
+  int rc = check_probe(W_R, x, B, Hq, d, d_model, dtype);
+  if (rc != PARALLAX_OK) return rc;
+  if (!rho) return fail(PARALLAX_ERR_INVALID_ARG, "null pointer argument (rho)");
+  if (!aligned(rho, 16)) return fail(PARALLAX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   const parallax::LaunchEvents ev = profile_events();
-  hipError_t e = parallax::launch_probe(W_R, x, rho, B, Hq * d, d_model, f32 ? 1 : 0, ev, stream);
+  hipError_t e = parallax::launch_probe(W_R, x, rho, B, Hq * d, d_model,
+                                        dtype == PARALLAX_F32 ? 1 : 0, ev, stream);
   profile_record(0, ev, e == hipSuccess);
   if (e != hipSuccess) return hip_fail(e, "probe launch");
   return PARALLAX_OK;
@@ -333,14 +384,32 @@ int parallax_decode_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype, 
   return PARALLAX_OK;
 }
 
+int parallax_probe_decode_plan(int B, int Hq, int Hkv, int d, int d_model, int max_ctx, int dtype,
+                               int* fused) {
+  int rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
+  if (rc != PARALLAX_OK) return rc;
+  if (d_model < 1) return fail(PARALLAX_ERR_INVALID_ARG, "d_model must be >= 1");
+  if (!fused) return fail(PARALLAX_ERR_INVALID_ARG, "null output pointer");
+  const Plan p = make_plan(B, Hq, Hkv, d, max_ctx, dtype);
+  *fused = fuse_probe(p, B, Hq, Hkv, d, d_model, dtype) ? 1 : 0;
+  return PARALLAX_OK;
+}
+
 }  // extern "C"
 
 namespace {
 
-// Shared by parallax_decode and parallax_softmax_decode (rho == nullptr).
-int decode_impl(const void* q, const float* rho, const void* k_cache, const void* v_cache,
-                const int* seq_lens, void* out, int B, int Hq, int Hkv, int d, int max_ctx,
-                int dtype, hipStream_t stream) {
+// A checked and planned decode call. The workspace holds `front` bytes for the
+// caller (the probe's rho in parallax_probe_decode), then the split states.
+struct DecodeCall {
+  parallax::DecodeArgs a;
+  Plan p;
+  void* front = nullptr;
+};
+
+int setup_decode(const void* q, const float* rho, const void* k_cache, const void* v_cache,
+                 const int* seq_lens, void* out, int B, int Hq, int Hkv, int d, int max_ctx,
+                 int dtype, size_t front_bytes, hipStream_t stream, DecodeCall& c) {
   int rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
   if (rc != PARALLAX_OK) return rc;
   if (!q || !k_cache || !v_cache || !seq_lens || !out)
@@ -350,7 +419,8 @@ int decode_impl(const void* q, const float* rho, const void* k_cache, const void
     return fail(PARALLAX_ERR_INVALID_ARG, "pointers must be 16-byte aligned (seq_lens 4-byte)");
 
   const Plan p = make_plan(B, Hq, Hkv, d, max_ctx, dtype);
-  parallax::DecodeArgs a;
+  c.p = p;
+  parallax::DecodeArgs& a = c.a;
   a.q = q;
   a.rho = rho;
   a.k = k_cache;
@@ -368,28 +438,50 @@ int decode_impl(const void* q, const float* rho, const void* k_cache, const void
   a.out_f32 = (dtype == PARALLAX_BF16) ? 0 : 1;
   a.scale_log2 = parallax::kLog2e / sqrtf((float)d);
 
-  if (p.splits > 1) {
-    const size_t states = (size_t)B * Hq * p.splits;
+  const size_t front = round_up(front_bytes, 256);
+  const size_t states = p.splits > 1 ? (size_t)B * Hq * p.splits : 0;
+  if (front + states > 0) {
     void* ws = nullptr;
-    rc = get_workspace(stream, states * sizeof(float4) + states * 2 * d * sizeof(float), &ws);
+    rc = get_workspace(stream, front + states * sizeof(float4) + states * 2 * d * sizeof(float),
+                       &ws);
     if (rc != PARALLAX_OK) return rc;
-    a.ml = (float4*)ws;
-    a.ap = (float*)((char*)ws + states * sizeof(float4));
+    c.front = front ? ws : nullptr;
+    if (states) {
+      a.ml = (float4*)((char*)ws + front);
+      a.ap = (float*)((char*)ws + front + states * sizeof(float4));
+    }
   }
+  return PARALLAX_OK;
+}
 
+// Decode (split-K pass) and, for split sequences, the merge.
+int launch_decode_call(const DecodeCall& c, int d, int dtype, int fused, hipStream_t stream) {
+  const parallax::DecodeArgs& a = c.a;
   parallax::LaunchEvents ev = profile_events();
   hipError_t e =
-      (p.kernel >= 2)
-          ? parallax::launch_decode_mfma(a, d, p.kernel == 3 ? 1 : 0, p.compact, ev, stream)
-          : parallax::launch_decode_generic(a, d, dtype == PARALLAX_F32 ? 1 : 0, ev, stream);
+      (c.p.kernel >= 2)
+          ? parallax::launch_decode_mfma(a, d, c.p.kernel == 3 ? 1 : 0, c.p.compact, fused, ev,
+                                         stream)
+          : parallax::launch_decode_generic(a, d, dtype == PARALLAX_F32 ? 1 : 0, fused, ev, stream);
   profile_record(1, ev, e == hipSuccess);
-  if (e == hipSuccess && p.splits > 1) {
+  if (e == hipSuccess && c.p.splits > 1) {
     ev = profile_events();
     e = parallax::launch_merge(a, d, ev, stream);
     profile_record(2, ev, e == hipSuccess);
   }
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return PARALLAX_OK;
+}
+
+// Shared by parallax_decode and parallax_softmax_decode (rho == nullptr).
+int decode_impl(const void* q, const float* rho, const void* k_cache, const void* v_cache,
+                const int* seq_lens, void* out, int B, int Hq, int Hkv, int d, int max_ctx,
+                int dtype, hipStream_t stream) {
+  DecodeCall c;
+  int rc = setup_decode(q, rho, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, d, max_ctx, dtype, 0,
+                        stream, c);
+  if (rc != PARALLAX_OK) return rc;
+  return launch_decode_call(c, d, dtype, 0, stream);
 }
 
 }  // namespace
@@ -409,6 +501,35 @@ int parallax_softmax_decode(const void* q, const void* k_cache, const void* v_ca
                             int max_ctx, int dtype, hipStream_t stream) {
   return decode_impl(q, nullptr, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, d, max_ctx, dtype,
                      stream);
+}
+
+int parallax_probe_decode(const void* W_R, const void* x, const void* q, const void* k_cache,
+                          const void* v_cache, const int* seq_lens, void* out, int B, int Hq,
+                          int Hkv, int d, int d_model, int max_ctx, int dtype, hipStream_t stream) {
+  int rc = check_probe(W_R, x, B, Hq, d, d_model, dtype);
+  if (rc != PARALLAX_OK) return rc;
+  rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
+  if (rc != PARALLAX_OK) return rc;
+  const bool fused = fuse_probe(make_plan(B, Hq, Hkv, d, max_ctx, dtype), B, Hq, Hkv, d, d_model,
+                                dtype);
+  DecodeCall c;
+  rc = setup_decode(q, nullptr, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, d, max_ctx, dtype,
+                    fused ? 0 : (size_t)B * Hq * d * sizeof(float), stream, c);
+  if (rc != PARALLAX_OK) return rc;
+  if (fused) {
+    c.a.W_R = W_R;
+    c.a.x = x;
+    c.a.d_model = d_model;
+    return launch_decode_call(c, d, dtype, 1, stream);
+  }
+  float* rho = (float*)c.front;
+  const parallax::LaunchEvents ev = profile_events();
+  hipError_t e = parallax::launch_probe(W_R, x, rho, B, Hq * d, d_model,
+                                        dtype == PARALLAX_F32 ? 1 : 0, ev, stream);
+  profile_record(0, ev, e == hipSuccess);
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  c.a.rho = rho;
+  return launch_decode_call(c, d, dtype, 0, stream);
 }
 
 }  // extern "C"
@@ -455,7 +576,7 @@ int prefill_impl(const void* q, const float* rho, const void* k_cache, const voi
     g.T = T;
     g.prefix = prefix_lens;
     const parallax::LaunchEvents ev = profile_events();
-    hipError_t e = parallax::launch_decode_generic(g, d, 1, ev, stream);
+    hipError_t e = parallax::launch_decode_generic(g, d, 1, 0, ev, stream);
     profile_record(3, ev, e == hipSuccess);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return PARALLAX_OK;

@@ -97,7 +97,71 @@ struct DecodeArgs {
   // 0 .. prefix[b / T] + b % T (prefix may be null: 0); seq_lens is unused.
   int T = 0;
   const int* prefix = nullptr;
+  // Probe fused into the decode (kernels launched with the fused flag): rho is
+  // not read from memory; each work item computes the rho of its query heads
+  // from W_R [Hq*d, d_model] and x [B, d_model] (storage type of q) in its
+  // prologue. d_model is a multiple of 16 / element size.
+  const void* W_R = nullptr;
+  const void* x = nullptr;
+  int d_model = 0;
 };
+
+// The probe fused into a decode work item: dst[r] = sum_c W[row0 + r][c] * xb[c]
+// for r < nrows (rows of d_model elements; xb = x of the item's sequence), fp32
+// accumulation, computed by the NT threads of the workgroup into LDS. A row
+// takes a group of LPR lanes (the power of two <= 16 that covers its 16-byte
+// pieces), lane i of the group reading pieces i, i + LPR, ...; each group
+// takes kProbeRowBatch rows at a time and issues their loads together (one
+// memory round trip per batch and piece step), then sums its lanes with xor
+// shuffles. The caller synchronises the workgroup before dst is read.
+constexpr int kProbeRowBatch = 8;
+template <bool F32IN, int NT>
+__device__ __forceinline__ void probe_rows(const void* W, const void* xb, int d_model,
+                                           size_t row0, int nrows, float* dst) {
+  constexpr int ESZ = F32IN ? 4 : 2;
+  constexpr int RB = kProbeRowBatch;
+  const int pieces = d_model * ESZ / 16;
+  int lpr = 16;
+  while (lpr > 1 && lpr / 2 >= pieces) lpr >>= 1;
+  const int ngroup = NT / lpr;
+  const int li = threadIdx.x & (lpr - 1), group = threadIdx.x / lpr;
+  const char* x8 = (const char*)xb;
+  const char* w8 = (const char*)W + row0 * (size_t)d_model * ESZ;
+  const size_t wrow = (size_t)d_model * ESZ;
+  for (int r0 = 0; r0 < nrows; r0 += ngroup * RB) {
+    float acc[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k) acc[k] = 0.f;
+    for (int pc = li; pc < pieces; pc += lpr) {
+      const u32x4 xv = *(const u32x4*)(x8 + (size_t)pc * 16);
+      u32x4 wv[RB];
+#pragma unroll
+      for (int k = 0; k < RB; ++k) {
+        const int r = r0 + group + ngroup * k;
+        wv[k] = r < nrows ? *(const u32x4*)(w8 + r * wrow + (size_t)pc * 16)
+                          : (u32x4){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int k = 0; k < RB; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (F32IN) {
+            acc[k] = fmaf(__uint_as_float(wv[k][i]), __uint_as_float(xv[i]), acc[k]);
+          } else {
+            acc[k] = fmaf(bf16_lo(wv[k][i]), bf16_lo(xv[i]), acc[k]);
+            acc[k] = fmaf(bf16_hi(wv[k][i]), bf16_hi(xv[i]), acc[k]);
+          }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      float a = acc[k];
+      for (int o = lpr >> 1; o >= 1; o >>= 1) a += __shfl_xor(a, o);
+      const int r = r0 + group + ngroup * k;
+      if (r < nrows && li == 0) dst[r] = a;
+    }
+  }
+}
 
 // Causal many-query forward: token t of sequence b is at cache position
 // prefix[b] + t and attends to cache rows 0 .. prefix[b] + t.
@@ -129,10 +193,13 @@ struct LaunchEvents {
 };
 
 // Internal launchers (one translation unit each). Return hipError_t.
-hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, LaunchEvents ev,
-                                 hipStream_t s);
+// fused = 1: the probe runs in each work item's prologue (DecodeArgs W_R, x,
+// d_model; rho unused).
+hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, int fused,
+                                 LaunchEvents ev, hipStream_t s);
 // compact = 1: compacted item numbering (workgroup items, B <= 256 only).
-hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, int compact,
+// fused = 1: workgroup items without compaction only.
+hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, int compact, int fused,
                               LaunchEvents ev, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, int d, LaunchEvents ev, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int d, LaunchEvents ev, hipStream_t s);

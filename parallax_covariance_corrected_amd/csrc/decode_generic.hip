@@ -2,7 +2,9 @@
 // any GQA group). Serves the fp32 path (decode, and prefill with one "sequence"
 // per token) and cross-checks the matrix-core kernel.
 //
-// One workgroup (4 waves) per (split, sequence, KV head, head block). Each key
+// One workgroup (4 waves) per (split, sequence, KV head, head block). With the
+// probe fused in, the workgroup first computes rho of its head block from W_R
+// and x into LDS (rho never goes through memory). Each key
 // is read by LPK lanes with one 16-byte load of K and one of V; the lanes of a
 // key reduce the score s = q.k and the probe p = k.rho with xor shuffles and
 // keep their own exact online state (m, l, S, A, P). States are merged across
@@ -50,7 +52,7 @@ __device__ __forceinline__ void combine(float& m, float& l, float& S, float* A, 
   m = M;
 }
 
-template <bool F32IN, int D, int GB>
+template <bool F32IN, int D, int GB, bool FUSED>
 __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   using E = Elem<F32IN>;
   constexpr int EPL = E::kPerLoad;   // elements per lane
@@ -87,14 +89,23 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   const int kg = lane / LPK, sub = lane % LPK;
   const int h0 = kvh * G + hb * GB;
 
+  const float* rsrc = a.rho;   // null: softmax only
+  if constexpr (FUSED) {
+    __shared__ float sR[GB * D];
+    probe_rows<F32IN, 256>(a.W_R, (const char*)a.x + (size_t)b * a.d_model * E::kSize, a.d_model,
+                           (size_t)h0 * D, GB * D, sR);
+    __syncthreads();
+    rsrc = sR;
+  }
   float qf[GB][EPL], rf[GB][EPL];
 #pragma unroll
   for (int h = 0; h < GB; ++h) {
     const size_t base = ((size_t)b * a.Hq + h0 + h) * D + sub * EPL;
     const u32x4 qw = *(const u32x4*)((const char*)a.q + base * E::kSize);
     E::unpack(qw, qf[h]);
+    const size_t rbase = FUSED ? (size_t)h * D + sub * EPL : base;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) rf[h][i] = a.rho ? a.rho[base + i] : 0.f;   // no rho: softmax only
+    for (int i = 0; i < EPL; ++i) rf[h][i] = rsrc ? rsrc[rbase + i] : 0.f;
   }
 
   float m[GB], l[GB], S[GB], A[GB][EPL], P[GB][EPL];
@@ -186,7 +197,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
   }
 }
 
-template <bool F32IN, int D>
+template <bool F32IN, int D, bool FUSED>
 hipError_t launch_d(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int GB = (G % 4 == 0) ? 4 : (G % 3 == 0) ? 3 : (G % 2 == 0) ? 2 : 1;
@@ -194,20 +205,27 @@ hipError_t launch_d(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), blk(256);
   switch (GB) {
-    case 4: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 4>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 3: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 3>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 2>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 1>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 4, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 3: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 3, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 2, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 1, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
   }
   return hipGetLastError();
 }
 
+template <bool FUSED>
+hipError_t launch_f(const DecodeArgs& a, int d, int f32_inputs, LaunchEvents ev, hipStream_t s) {
+  if (f32_inputs)
+    return d == 64 ? launch_d<true, 64, FUSED>(a, ev, s) : launch_d<true, 128, FUSED>(a, ev, s);
+  return d == 64 ? launch_d<false, 64, FUSED>(a, ev, s) : launch_d<false, 128, FUSED>(a, ev, s);
+}
+
 }  // namespace
 
-hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, LaunchEvents ev,
-                                 hipStream_t s) {
-  if (f32_inputs) return d == 64 ? launch_d<true, 64>(a, ev, s) : launch_d<true, 128>(a, ev, s);
-  return d == 64 ? launch_d<false, 64>(a, ev, s) : launch_d<false, 128>(a, ev, s);
+hipError_t launch_decode_generic(const DecodeArgs& a, int d, int f32_inputs, int fused,
+                                 LaunchEvents ev, hipStream_t s) {
+  if (fused && (a.T > 0 || !a.W_R || !a.x)) return hipErrorInvalidValue;
+  return fused ? launch_f<true>(a, d, f32_inputs, ev, s) : launch_f<false>(a, d, f32_inputs, ev, s);
 }
 
 }  // namespace parallax

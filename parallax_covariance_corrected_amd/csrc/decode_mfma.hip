@@ -23,6 +23,8 @@
 // item of the split-major order instead, so the workgroups that find nothing
 // form one run at the end of the grid rather than being interleaved with
 // working ones.
+// With the probe fused in (workgroup items only), the workgroup computes rho
+// of its head block from W_R and x into LDS while its first K/V tiles load.
 // A sequence that fits in one chunk gets its output written directly;
 // otherwise each non-empty split writes its partial state (m, l, S, A, P)
 // and the merge kernel combines them.
@@ -190,8 +192,9 @@ __device__ __forceinline__ bool compact_item(const DecodeArgs& a, int item, int 
   return false;
 }
 
-template <int D, int GH, bool WAVE_ITEM, int NW, bool CORR, bool COMPACT>
+template <int D, int GH, bool WAVE_ITEM, int NW, bool CORR, bool COMPACT, bool FUSED>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+  static_assert(!FUSED || (CORR && !WAVE_ITEM), "the fused probe serves workgroup items");
   using L = Layout<GH, CORR>;
   using C = KV<D>;
   constexpr int NC = C::NC, TPL = C::TPL, ROW = C::ROW, NSET = L::NSET;
@@ -257,6 +260,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NBS = WAVE_ITEM ? NW : 1;
   const int bslot = WAVE_ITEM ? wave : 0;
   __shared__ u32x4 sB[NBS][NC][64];
+  const float* rsrc = a.rho;
+  if constexpr (FUSED) {
+    __shared__ __attribute__((aligned(16))) float sR[GH * D];
+    probe_rows<false, NW * 64>(a.W_R, (const uint16_t*)a.x + (size_t)b * a.d_model, a.d_model,
+                               (size_t)h0 * D, GH * D, sR);
+    __syncthreads();
+    rsrc = sR;
+  }
   if (WAVE_ITEM || wave == 0) {
     const size_t bh = (size_t)b * a.Hq + h0 + (qi < GH ? qi : 0);
 #pragma unroll
@@ -266,8 +277,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
       if (qi < GH && quad == 0) {
         v = *(const u32x4*)((const uint16_t*)a.q + off);
       } else if (CORR && qi < GH && (quad == 1 || quad == 2)) {
-        const float4 r0 = *(const float4*)(a.rho + off);
-        const float4 r1 = *(const float4*)(a.rho + off + 4);
+        const size_t roff = FUSED ? (size_t)qi * D + 32 * c + 8 * grp : off;
+        const float4 r0 = *(const float4*)(rsrc + roff);
+        const float4 r1 = *(const float4*)(rsrc + roff + 4);
         const float r[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -482,7 +494,7 @@ int head_block(int G) {
   return 1;
 }
 
-template <int D, bool WI, int NW, bool CORR, bool CP>
+template <int D, bool WI, int NW, bool CORR, bool CP, bool FU = false>
 hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int GH = head_block(G);
@@ -491,10 +503,10 @@ hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   if (grid > 0x7fffffffu || items > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), blk(NW * 64);
   switch (GH) {
-    case 4: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 4, WI, NW, CORR, CP>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 3: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 3, WI, NW, CORR, CP>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 2, WI, NW, CORR, CP>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 1, WI, NW, CORR, CP>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 4, WI, NW, CORR, CP, FU>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 3: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 3, WI, NW, CORR, CP, FU>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 2, WI, NW, CORR, CP, FU>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    default: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 1, WI, NW, CORR, CP, FU>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
   }
   return hipGetLastError();
 }
@@ -502,6 +514,11 @@ hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
 template <bool CORR>
 hipError_t launch_d(const DecodeArgs& a, int d, int wave_items, int compact, LaunchEvents ev,
                     hipStream_t s) {
+  if constexpr (CORR) {
+    if (a.W_R)
+      return d == 64 ? launch_dw<64, false, 4, true, false, true>(a, ev, s)
+                     : launch_dw<128, false, 4, true, false, true>(a, ev, s);
+  }
   if (wave_items)
     return d == 64 ? launch_dw<64, true, 4, CORR, false>(a, ev, s)
                    : launch_dw<128, true, 4, CORR, false>(a, ev, s);
@@ -516,12 +533,20 @@ hipError_t launch_d(const DecodeArgs& a, int d, int wave_items, int compact, Lau
 
 bool decode_mfma_supported(int d, int G) { return (d == 64 || d == 128) && G >= 1; }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, int compact,
+hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, int compact, int fused,
                               LaunchEvents ev, hipStream_t s) {
   if (compact && (wave_items || a.B > 64 * kCompactGroups)) return hipErrorInvalidValue;
+  if (fused) {
+    if (wave_items || compact || !a.W_R || !a.x) return hipErrorInvalidValue;
+    DecodeArgs f = a;
+    f.rho = nullptr;
+    return launch_d<true>(f, d, 0, 0, ev, s);
+  }
   // rho == nullptr selects plain softmax attention (no correction branch).
-  return a.rho ? launch_d<true>(a, d, wave_items, compact, ev, s)
-               : launch_d<false>(a, d, wave_items, compact, ev, s);
+  DecodeArgs u = a;
+  u.W_R = nullptr;
+  return u.rho ? launch_d<true>(u, d, wave_items, compact, ev, s)
+               : launch_d<false>(u, d, wave_items, compact, ev, s);
 }
 
 }  // namespace parallax

@@ -14,7 +14,7 @@
 // before their MFMAs, and reduce through LDS in a fixed order. Rows past B
 // read zeros (buffer range). Larger batches (B > 64): an LDS-tiled GEMM with
 // 128 x 128 tiles (below), where operand reuse across waves pays for staging.
-// fp32 kernel: one thread per output, a plain dot product.
+// fp32 kernel: one wave per output, a plain dot product.
 #include <type_traits>
 
 #include "common.h"
@@ -225,18 +225,32 @@ __global__ __launch_bounds__(kGThreads) void probe_gemm_kernel(const uint16_t* _
     }
 }
 
+// fp32: one wave per output rho[row][col]; lane l takes elements l, l + 64, ...
+// of the dot product (each load instruction reads 256 contiguous bytes of the
+// W_R row and of x), four accumulators, then a wave sum.
 __global__ __launch_bounds__(256) void probe_f32_kernel(const float* __restrict__ W,
                                                         const float* __restrict__ x,
                                                         float* __restrict__ rho, int B, int N,
                                                         int K) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)B * N) return;
+  const int lane = threadIdx.x & 63;
+  const size_t idx = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (idx >= (size_t)B * N) return;   // whole waves
   const int row = (int)(idx / N), col = (int)(idx % N);
   const float* w = W + (size_t)col * K;
   const float* xr = x + (size_t)row * K;
-  float s = 0.f;
-  for (int k = 0; k < K; ++k) s = fmaf(w[k], xr[k], s);
-  rho[idx] = s;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int k = lane;
+  for (; k + 192 < K; k += 256) {
+    s0 = fmaf(w[k], xr[k], s0);
+    s1 = fmaf(w[k + 64], xr[k + 64], s1);
+    s2 = fmaf(w[k + 128], xr[k + 128], s2);
+    s3 = fmaf(w[k + 192], xr[k + 192], s3);
+  }
+  for (; k < K; k += 64) s0 = fmaf(w[k], xr[k], s0);
+  float s = (s0 + s1) + (s2 + s3);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) rho[idx] = s;
 }
 
 }  // namespace
@@ -245,7 +259,7 @@ hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, 
                         int f32_inputs, LaunchEvents ev, hipStream_t s) {
   if (f32_inputs) {
     const size_t total = (size_t)B * N;
-    const size_t grid = (total + 255) / 256;
+    const size_t grid = (total + 3) / 4;
     if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
     hipExtLaunchKernelGGL(probe_f32_kernel, dim3(grid), dim3(256), 0, s, ev.start, ev.stop, 0,
                           (const float*)W, (const float*)x, rho, B, N, K);

@@ -57,6 +57,62 @@ def test_probe_rejects_bad_arguments(L, args, code):
     assert L.parallax_last_error().decode()
 
 
+def _probe_decode(L, *, W=16, x=16, q=16, k=16, v=16, lens=16, out=16, B=2, Hq=4, Hkv=2, d=128,
+                  d_model=64, max_ctx=64, dtype=pb.BF16):
+    return L.parallax_probe_decode(W, x, q, k, v, lens, out, B, Hq, Hkv, d, d_model, max_ctx,
+                                   dtype, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(W=0), pb.ERR_INVALID_ARG, "null"),
+    (dict(x=24), pb.ERR_INVALID_ARG, "aligned"),
+    (dict(d_model=60), pb.ERR_INVALID_ARG, "multiple of 8"),
+    (dict(d_model=0), pb.ERR_INVALID_ARG, ">= 1"),
+    (dict(Hq=3, Hkv=2), pb.ERR_INVALID_ARG, "multiple"),
+    (dict(d=96), pb.ERR_UNSUPPORTED, "64 or 128"),
+    (dict(dtype=7), pb.ERR_UNSUPPORTED, "dtype"),
+    (dict(q=0), pb.ERR_INVALID_ARG, "null"),
+    (dict(lens=18), pb.ERR_INVALID_ARG, "aligned"),
+    (dict(max_ctx=1 << 24), pb.ERR_UNSUPPORTED, "max_ctx"),
+])
+def test_probe_decode_rejects_bad_arguments(L, kw, code, msg):
+    assert _probe_decode(L, **kw) == code
+    assert msg in L.parallax_last_error().decode()
+
+
+def test_probe_decode_plan():
+    # the tiny fp32 workload: W_R is 32 KB per work item, the probe runs inside the decode
+    assert pb.probe_decode_plan(1, 2, 2, 64, 128, 128, pb.F32)
+    # the bf16 workloads (d_model 2048 / 2560): a separate probe launch
+    for shape in [(16, 16, 8, 128, 2048, 4096), (1, 16, 8, 128, 2048, 32768),
+                  (2048, 16, 8, 128, 2048, 128), (64, 32, 8, 128, 2560, 32768)]:
+        assert not pb.probe_decode_plan(*shape, pb.BF16)
+    # small d_model and few items: fused (32 KiB per item up to 16 MiB in all,
+    # 64 KiB per item up to 8 MiB); more: separate
+    assert pb.probe_decode_plan(4, 16, 8, 128, 64, 1024, pb.BF16)          # 32 KiB x 256
+    assert pb.probe_decode_plan(1, 16, 8, 128, 128, 128, pb.BF16)          # 64 KiB x 8
+    assert not pb.probe_decode_plan(4, 16, 8, 128, 128, 1024, pb.BF16)     # 64 KiB x 256
+    assert not pb.probe_decode_plan(1, 16, 8, 128, 256, 128, pb.BF16)      # 128 KiB
+    assert not pb.probe_decode_plan(256, 16, 8, 128, 64, 1024, pb.BF16)
+    # the generic kernel (fp32): up to 128 KiB per item, 8 MiB in all
+    assert pb.probe_decode_plan(4, 2, 2, 64, 512, 1024, pb.F32)            # 128 KiB x 64
+    assert not pb.probe_decode_plan(4, 2, 2, 64, 1024, 128, pb.F32)
+    # fp32 rows of d_model elements must be whole 16-byte pieces
+    assert not pb.probe_decode_plan(1, 2, 2, 64, 130, 128, pb.F32)
+    with pb.options(fuse=1):
+        assert not pb.probe_decode_plan(1, 2, 2, 64, 128, 128, pb.F32)
+    with pb.options(fuse=2):
+        assert pb.probe_decode_plan(16, 16, 8, 128, 2048, 4096, pb.BF16)
+        assert pb.get_option(pb.OPT_FUSE) == 2
+        # one wave per item (many short sequences) and the compacted numbering
+        # (ragged batch in a large cache) keep the separate probe
+        assert pb.decode_plan(2048, 16, 8, 128, 128)[2] == 3
+        assert not pb.probe_decode_plan(2048, 16, 8, 128, 2048, 128, pb.BF16)
+        assert not pb.probe_decode_plan(64, 32, 8, 128, 2560, 32768, pb.BF16)
+    assert pb.get_option(pb.OPT_FUSE) == 0
+    assert pb.lib().parallax_set_option(pb.OPT_FUSE, 3) == pb.ERR_INVALID_ARG
+
+
 def _prefill(L, *, q=16, rho=16, k=16, v=16, pre=16, out=16, B=2, T=8, Hq=4, Hkv=2, d=128,
              max_ctx=64, dtype=pb.BF16):
     return L.parallax_prefill(q, rho, k, v, pre, out, B, T, Hq, Hkv, d, max_ctx, dtype, None)
