@@ -149,15 +149,15 @@ struct Plan {
 // probe launch (a few microseconds whatever its size) only where the reads per
 // item and in total stay small. Limits from timing whole steps both ways over
 // batch 1-64 x d_model 64-2048 x context 128-4096 (Hq 16, Hkv 8, d 128, bf16;
-// and fp32 shapes): on the matrix-core kernel fusing was 3-28% faster at
-// 32 KiB per item and 2-12% at 64 KiB per item with up to 8 MiB in all, and
-// slower beyond (up to 2.4x at 1 MiB per item); on the generic kernel, whose
-// decode is slower and hides more of the prologue, 13-25% faster up to
-// 128 KiB per item.
+// and fp32 shapes), three runs: on the matrix-core kernel the fused step took
+// 0.74-0.98x the separate one at 32 KiB of W_R per item (up to 16 MiB in
+// all), 0.88-1.17x at 64 KiB, and more beyond (up to 2.6x at 1 MiB per item);
+// on the generic kernel, whose decode is slower and hides more of the
+// prologue, 0.74-0.94x up to 128 KiB per item.
 struct FuseLimit {
   long long item_bytes, total_bytes;
 };
-constexpr FuseLimit kFuseMfma[] = {{32LL << 10, 16LL << 20}, {64LL << 10, 8LL << 20}};
+constexpr FuseLimit kFuseMfma[] = {{32LL << 10, 16LL << 20}};
 constexpr FuseLimit kFuseGeneric[] = {{128LL << 10, 8LL << 20}};
 
 int esize(int dtype) { return dtype == PARALLAX_F32 ? 4 : 2; }
