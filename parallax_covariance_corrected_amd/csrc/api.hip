@@ -243,10 +243,10 @@ bool fuse_probe(const Plan& p, int B, int Hq, int Hkv, int d, int d_model, int d
   if (g_opt_fuse == 2) return true;
   const int G = Hq / Hkv;
   const int GH = head_block(G, p.kernel >= 2);
-  const long long item_bytes = (long long)GH * d * d_model * es;
-  const long long total = (long long)B * Hkv * (G / GH) * p.splits * item_bytes;
+  const long long item_bytes = (long long)GH * d * d_model * es;   // > 0
+  const long long items = (long long)B * Hkv * (G / GH) * p.splits;
   auto within = [&](const FuseLimit& f) {
-    return item_bytes <= f.item_bytes && total <= f.total_bytes;
+    return item_bytes <= f.item_bytes && items <= f.total_bytes / item_bytes;
   };
   if (p.kernel >= 2) return std::any_of(std::begin(kFuseMfma), std::end(kFuseMfma), within);
   return std::any_of(std::begin(kFuseGeneric), std::end(kFuseGeneric), within);
