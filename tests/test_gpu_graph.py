@@ -60,3 +60,45 @@ def test_decode_step_in_a_graph_replays_exactly():
         again = eager(devs[(i + 1) % 3])
         assert torch.equal(again, refs[(i + 1) % 3])
     say("graph decode: 6 replays equal to eager")
+
+
+@pytest.mark.parametrize("fuse", [1, 2])
+def test_one_call_step_in_a_graph_replays_exactly(fuse):
+    """parallax_probe_decode captured into a graph, with the probe in a launch
+    of its own (rho in the library's workspace) and fused into the decode."""
+    wl = WORKLOADS[2].scaled(B=4, ctx=1500, d_model=64)
+    sets = [make_inputs(wl, seed) for seed in (21, 22, 23)]
+    devs = [Device(s, pad=0.0) for s in sets]
+    say(f"[case] graph probe_decode fuse={fuse} B={wl.B} ctx={wl.ctx}")
+    with pb.options(fuse=fuse):
+        assert pb.probe_decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.d_model, wl.capacity) == (fuse == 2)
+
+        def eager(dv):
+            out = pb.probe_decode(dv.W_R, dv.x, dv.q, dv.K, dv.V, dv.seq_lens)
+            torch.cuda.synchronize()
+            return out.clone()
+
+        refs = [eager(dv) for dv in devs]
+        st = Device(sets[0], pad=0.0)
+        out = torch.empty((wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device="cuda")
+        s = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):   # size this stream's workspace before capture
+            pb.probe_decode(st.W_R, st.x, st.q, st.K, st.V, st.seq_lens, out=out)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            pb.probe_decode(st.W_R, st.x, st.q, st.K, st.V, st.seq_lens, out=out)
+        torch.cuda.synchronize()
+        for rep in range(6):
+            i = rep % 3
+            for name in ("x", "W_R", "q", "K", "V", "seq_lens"):
+                getattr(st, name).copy_(getattr(devs[i], name))
+            out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, refs[i]), f"replay {rep} (input set {i}) differs from eager"
+            again = eager(devs[(i + 1) % 3])
+            assert torch.equal(again, refs[(i + 1) % 3])
+    say(f"graph probe_decode fuse={fuse}: 6 replays equal to eager")
