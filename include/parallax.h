@@ -102,7 +102,10 @@ int parallax_probe(const void* W_R, const void* x, float* rho,
  * process ends; it grows stream-ordered on `stream` (hipMallocAsync, old
  * buffer hipFreeAsync'd). Growing is refused (PARALLAX_ERR_NO_MEMORY) while
  * `stream` is being captured into a graph: make one call of the largest shape
- * on that stream before capturing.
+ * on that stream before capturing. The cache is keyed by the stream handle: a
+ * stream with library work still pending must be synchronised before it is
+ * destroyed, since a stream created afterwards may receive the same handle and
+ * would share the workspace.
  */
 int parallax_decode(const void* q, const float* rho, const void* k_cache,
                     const void* v_cache, const int* seq_lens, void* out,
