@@ -127,7 +127,7 @@ def test_long_context_splits_fused():
     _both_paths(s, "long ctx d_model=128")
 
 
-@pytest.mark.parametrize("idx", [2, 4])
+@pytest.mark.parametrize("idx", [2, 4, 5])
 def test_full_size_separate_plan_equals_probe_then_decode(idx):
     """On the bf16 workloads the plan keeps the probe separate; the result is
     then bit for bit that of parallax_probe followed by parallax_decode (same
