@@ -154,3 +154,25 @@ def test_full_size_separate_plan_equals_probe_then_decode(idx):
         d = rel_l2(to64(f), to64(one))
         say(f"full size forced fused vs separate rel {d:.3e}")
         assert d <= 1e-5
+
+
+def test_random_shapes_both_placements():
+    """Twenty seeded random shapes: batch 1-9, G in 1..8, d in {64, 128},
+    d_model a multiple of 8 up to 600, cache 1-700 keys with random lengths
+    (zero allowed), forced chunk sizes; probe fused and separate against the
+    oracle."""
+    rng = np.random.default_rng(2026)
+    for case in range(20):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.integers(1, 4))
+        G = int(rng.integers(1, 9))
+        B = int(rng.integers(1, 10))
+        cap = int(rng.integers(1, 701))
+        d_model = 8 * int(rng.integers(1, 76))
+        lens = [int(x) for x in rng.integers(0, cap + 1, size=B)]
+        chunk = int(rng.choice([0, 64, 128, 256]))
+        wl = WORKLOADS[2].scaled(B=B, Hq=G * Hkv, Hkv=Hkv, d=d, ctx=cap, d_model=d_model,
+                                 wr_std=0.05)
+        s = make_inputs(wl, 100 + case, lengths=lens)
+        with pb.options(chunk=chunk):
+            _both_paths(s, f"random case {case} chunk={chunk}")
