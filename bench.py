@@ -332,16 +332,21 @@ def run_workload(args, wl_id: int, emit: bool = True):
 
 
 def run_sweep(args):
-    """Batch x context sweep at Hq=16, Hkv=8, d=128 bf16 (decode split-K pass +
-    merge, rotated K/V sets so that every rep reads cold data); one JSON line
-    per point. GB/s counts K/V, q, rho, out and seq_lens; `pct_peak` is over
-    the whole call (both launches), `kernel_pct_peak` over the decode kernel's
-    own duration (per-launch events)."""
+    """Batch x context sweep at Hq=16, Hkv=8, d=128, d_model=2048, bf16. Per point,
+    on rotated K/V sets (so that every call reads cold data): the decode call
+    (split-K pass + merge) timed over 100 calls after 20 warm-up calls, each call
+    bracketed by its own events (median, p10, p90), and the decode kernel's own
+    duration (per-launch events); the probe alone and the whole step through
+    parallax_probe_decode (mean over 100 steps); the share of the correction in
+    the output, ||C rho|| / ||out||. One JSON line per point. GB/s counts K/V,
+    q, rho, out and seq_lens; `pct_peak` is over the decode call's median,
+    `kernel_pct_peak` over the decode kernel's own duration."""
     import torch
     from parallax_covariance_corrected_amd import binding as pb
     from parallax_covariance_corrected_amd.workloads import sweep_points
 
     dev = "cuda"
+    warm, reps, d_model = 20, 100, 2048
     max_bytes = args.sweep_max_gib << 30
     for (B, ctx) in sweep_points(max_bytes // 2 if args.sweep_max_gib else 64 << 30):
         kv = 2 * B * ctx * 8 * 128 * 2
@@ -352,43 +357,67 @@ def run_sweep(args):
             K = torch.randn((B, 8, ctx, 128), generator=g, device=dev, dtype=torch.bfloat16)
             V = torch.randn((B, 8, ctx, 128), generator=g, device=dev, dtype=torch.bfloat16)
             sets.append((K, V))
+        x = torch.randn((B, d_model), generator=g, device=dev).to(torch.bfloat16)
+        W_R = (torch.randn((16 * 128, d_model), generator=g, device=dev) * 0.02).to(torch.bfloat16)
         q = torch.randn((B, 16, 128), generator=g, device=dev).to(torch.bfloat16)
-        rho = torch.randn((B, 16, 128), generator=g, device=dev) * 0.1
+        rho = pb.probe(W_R, x, 16, 128)
         lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
         out = torch.empty((B, 16, 128), dtype=torch.bfloat16, device=dev)
-        for i in range(5):
+
+        def call(i):
             K, V = sets[i % nsets]
             pb.decode(q, rho, K, V, lens, out=out)
+
+        for i in range(warm):
+            call(i)
         torch.cuda.synchronize()
-        reps = 30
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(reps):
-            K, V = sets[i % nsets]
-            pb.decode(q, rho, K, V, lens, out=out)
-        e1.record()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            call(i)
+            b.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        p10, med, p90 = (t[int(f * (reps - 1))] for f in (0.1, 0.5, 0.9))
         # the same calls again with per-launch events: the decode kernel alone
         pb.profile_reset()
         with pb.options(profile=1):
             for i in range(reps):
-                K, V = sets[i % nsets]
-                pb.decode(q, rho, K, V, lens, out=out)
+                call(i)
             torch.cuda.synchronize()
             kms, kn = pb.profile_read(pb.KERNEL_DECODE)
-        kus = kms / kn * 1e3
+            for i in range(reps):
+                pb.probe(W_R, x, 16, 128, out=rho)
+            torch.cuda.synchronize()
+            pms, pn = pb.profile_read(pb.KERNEL_PROBE)
+        kus, pus = kms / kn * 1e3, pms / pn * 1e3
+
+        def step(i):
+            K, V = sets[i % nsets]
+            pb.probe_decode(W_R, x, q, K, V, lens, out=out)
+
+        step_us = timed_steps(step, reps, warm=5)
+        par = pb.decode(q, rho, *sets[0], lens, out_dtype=torch.float32)
+        soft = pb.softmax_decode(q, *sets[0], lens, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        corr = float((par - soft).norm() / par.norm())
         byts = kv + B * 16 * 128 * (2 + 4 + 2) + B * 4
         chunk, splits, kern = pb.decode_plan(B, 16, 8, 128, ctx)
+
+        def pct(us):
+            return round(100 * byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)
         print(json.dumps({"sweep": True, "B": B, "ctx": ctx, "plan": [chunk, splits, kern],
-                          "us_per_step": round(us, 2),
-                          "tokens_per_s": round(B / (us * 1e-6), 1),
-                          "gbps": round(byts / (us * 1e-6) / 1e9, 1),
-                          "pct_peak": round(100 * byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
-                          "kernel_us": round(kus, 2),
-                          "kernel_pct_peak": round(100 * byts / (kus * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)}),
+                          "us_per_step": round(med, 2), "p10_us": round(p10, 2),
+                          "p90_us": round(p90, 2),
+                          "tokens_per_s": round(B / (med * 1e-6), 1),
+                          "gbps": round(byts / (med * 1e-6) / 1e9, 1),
+                          "pct_peak": pct(med),
+                          "kernel_us": round(kus, 2), "kernel_pct_peak": pct(kus),
+                          "probe_us": round(pus, 2), "probe_decode_step_us": round(step_us, 2),
+                          "correction_to_output": round(corr, 4)}),
               flush=True)
-        del sets, q, rho, lens, out
+        del sets, q, rho, lens, out, x, W_R, par, soft
         torch.cuda.empty_cache()
 
 
