@@ -350,7 +350,10 @@ def run_sweep(args):
     max_bytes = args.sweep_max_gib << 30
     for (B, ctx) in sweep_points(max_bytes // 2 if args.sweep_max_gib else 64 << 30):
         kv = 2 * B * ctx * 8 * 128 * 2
-        nsets = max(1, min(3, (768 << 20) // kv + 1))
+        # At least two sets (three below 768 MB) alternate, so that between two
+        # calls on one set at least 768 MB of other K/V streams through the
+        # 256 MB last-level cache: every call reads its K/V cold.
+        nsets = max(2, min(3, (768 << 20) // kv + 1))
         g = torch.Generator(device=dev).manual_seed(B * 100003 + ctx)
         sets = []
         for _ in range(nsets):
