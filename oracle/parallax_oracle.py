@@ -25,7 +25,9 @@ Readings where the pages are silent (each pinned by a test, see tests/):
 scores are q.k/sqrt(d); the covariance is C = sum_j w_j (v_j - vbar)(k_j - kbar)^T
 (value rows, key columns) so that C rho contracts rho with keys; rho is per
 query head; query head h reads KV head floor(h / (Hq/Hkv)); a sequence of
-length 0 gives an all-zero output.
+length 0 gives an all-zero output; a length outside [0, rows in the cache] is
+clamped into it (the decode library's documented treatment of a caller
+error), so a negative length also gives zeros.
 
 Everything is float64; inputs are the exact values the GPU receives (bf16 or
 fp32), upcast without rounding.
@@ -35,7 +37,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["probe", "softmax_weights", "weighted_means", "kv_covariance",
-           "decode_head", "decode", "decode_heads", "kv_head_of", "prefill", "prefill_rows"]
+           "decode_head", "decode", "decode_heads", "kv_head_of", "clamp_len", "prefill",
+           "prefill_rows"]
 
 
 def _f64(a) -> np.ndarray:
@@ -110,10 +113,21 @@ def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
+def clamp_len(n: int, rows: int) -> int:
+    """A sequence length as the decode uses it: lengths above the rows the cache
+    holds (max_ctx for a padded cache) count as all of them, and a negative
+    length counts as 0, i.e. an empty cache and a zero output (the n = 0
+    convention of decode_head)."""
+    return max(0, min(int(n), int(rows)))
+
+
 def _seq_kv(K_parts, V_parts, b, g, n):
     """K, V rows 0..n-1 of KV head g of sequence b, from either per-sequence
-    [Hkv, n_b, d] lists or a padded [B, Hkv, max_ctx, d] cache."""
-    return K_parts[b][g][:n], V_parts[b][g][:n]
+    [Hkv, n_b, d] lists or a padded [B, Hkv, max_ctx, d] cache; n is clamped
+    to the rows present (clamp_len)."""
+    Kg, Vg = K_parts[b][g], V_parts[b][g]
+    n = clamp_len(n, Kg.shape[0])
+    return Kg[:n], Vg[:n]
 
 
 def decode(q, rho, K_parts, V_parts, seq_lens, Hkv: int) -> np.ndarray:
@@ -136,14 +150,18 @@ def decode(q, rho, K_parts, V_parts, seq_lens, Hkv: int) -> np.ndarray:
 
 
 def decode_heads(q, rho, K_parts, V_parts, seq_lens, Hkv: int, pairs) -> np.ndarray:
-    """decode() restricted to the listed (b, h) pairs -> [len(pairs), d]."""
+    """decode() restricted to the listed (b, h) pairs -> [len(pairs), d]: pair
+    (b, h) reads the length of sequence b and KV head kv_head_of(h), exactly
+    as decode() does for that output row."""
     Hq = q.shape[1]
+    lens = [int(n) for n in _f64(seq_lens)]
     res = []
     for b, h in pairs:
-        n = int(seq_lens[b])
         g = kv_head_of(h, Hq, Hkv)
-        Kb, Vb = _seq_kv(K_parts, V_parts, b, g, n)
+        Kb, Vb = _seq_kv(K_parts, V_parts, b, g, lens[b])
         res.append(decode_head(q[b, h], rho[b, h], Kb, Vb))
+    if not res:
+        return np.zeros((0, q.shape[2]))
     return np.stack(res)
 
 

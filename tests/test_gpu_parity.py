@@ -98,15 +98,32 @@ def test_bf16_workloads_reduced(name, seed):
     _run_full_check(s, f"{name} seed{seed}")
 
 
-# ------------------------------------------------------------------ full sizes, sampled heads
-FULL = {"gqa_mid_ctx": (2, 24), "large_batch": (4, 48), "ragged_G4": (5, 24)}
+# ------------------------------------------------------------------ full sizes
+def heads_of_every_sequence(s, per_seq: int = 4, seed: int = 0):
+    """per_seq distinct query heads of every sequence (seeded), plus the first
+    and last head of the longest one."""
+    r = np.random.default_rng(seed)
+    B, Hq = s.wl.B, s.wl.Hq
+    pairs = {(b, int(h)) for b in range(B) for h in r.choice(Hq, min(per_seq, Hq), replace=False)}
+    longest = int(np.argmax(s.seq_lens.numpy()))
+    pairs |= {(longest, 0), (longest, Hq - 1)}
+    return sorted(pairs)
+
+
+# workload -> None (every (sequence, head) pair) or heads per sequence
+FULL = {"gqa_mid_ctx": (2, None), "large_batch": (4, None), "ragged_G4": (5, 4)}
 
 
 @pytest.mark.parametrize("name", list(FULL))
-def test_bf16_workloads_full_size_sampled(name):
-    idx, k = FULL[name]
+def test_bf16_workloads_full_size(name):
+    """The bf16 workloads at full size in the default launch plan: every output
+    row of the mid-context (256 rows) and large-batch (32768 rows) workloads,
+    and 4 query heads of each of the 64 ragged sequences (258 rows)."""
+    idx, per_seq = FULL[name]
     s = make_inputs(WORKLOADS[idx], 0)
-    pairs = sample_pairs(s, k)
+    pairs = None if per_seq is None else heads_of_every_sequence(s, per_seq)
+    if pairs is not None:
+        assert {b for b, _ in pairs} == set(range(s.wl.B)) and len(pairs) >= 256
     _run_full_check(s, f"{name} full", pairs=pairs, wr_zero_too=False)
 
 
@@ -144,19 +161,23 @@ def test_edge_lengths(d, Hq, Hkv, dtype):
     assert np.all(o[0] == 0.0)
 
 
-def test_zero_length_gives_zero_and_clamps_long_lengths():
-    wl = WORKLOADS[2].scaled(B=3, ctx=200, d_model=64, Hq=4, Hkv=2)
-    s = make_inputs(wl, 5, lengths=[0, 200, 200])
-    say("[case] zero length / clamp")
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_zero_length_gives_zero_and_clamps_long_lengths(chunk):
+    """Length 0 and a negative length give a zero output; a length above
+    max_ctx counts as max_ctx (one split, and four splits with the merge)."""
+    wl = WORKLOADS[2].scaled(B=4, ctx=200, d_model=64, Hq=4, Hkv=2)
+    s = make_inputs(wl, 5, lengths=[0, 200, 200, 200])
+    say(f"[case] zero length / clamp chunk={chunk}")
     dev = Device(s)
     # sequence 2 is a copy of sequence 1 whose length 1000 exceeds max_ctx = 200
     for t in (dev.K, dev.V, dev.q, dev.x):
         t[2].copy_(t[1])
-    dev.seq_lens = torch.tensor([0, 200, 1000], dtype=torch.int32, device="cuda")
+    dev.seq_lens = torch.tensor([0, 200, 1000, -7], dtype=torch.int32, device="cuda")
     rho = dev.probe()
-    out = to64(dev.decode(rho, out_dtype=torch.float32))
+    with pb.options(chunk=chunk):
+        out = to64(dev.decode(rho, out_dtype=torch.float32))
     torch.cuda.synchronize()
-    assert np.all(out[0] == 0.0)
+    assert np.all(out[0] == 0.0) and np.all(out[3] == 0.0)
     np.testing.assert_array_equal(out[1], out[2])   # same data, length clamped to 200
 
 
@@ -271,8 +292,8 @@ def test_softmax_only_variant(Hq, Hkv, dtype, kernel, items):
 
 def test_workspace_grows_across_shapes_and_streams():
     """The per-stream split-K workspace grows when a larger shape arrives and
-    its arrival counters return to zero after every call (smaller shapes after
-    larger ones, a second stream, repeated calls)."""
+    stays right for every shape after that (smaller shapes after larger ones,
+    a second stream with its own workspace, repeated calls)."""
     cases = [(2, 900, [900, 700]), (5, 4000, [4000, 3999, 2500, 1, 130]), (3, 1500, [1500, 20, 1499])]
     side = torch.cuda.Stream()
     for rep in range(2):

@@ -253,9 +253,65 @@ def pin_gqa_equals_mha():
                                oracle.decode(q, rho, Kr, Vr, lens, Hq), atol=0, rtol=0)
 
 
+def _ragged_gqa_case(seed, pad=np.nan):
+    """A ragged GQA batch (Hq 6, Hkv 2, lengths 9, 0, 1, 13 in a 16-row cache)
+    in both layouts the oracle accepts: per-sequence [Hkv, n_b, d] arrays and a
+    padded [B, Hkv, 16, d] cache whose rows past each length hold `pad`."""
+    r = _rng(seed)
+    B, Hq, Hkv, d, cap = 4, 6, 2, 5, 16
+    lens = [9, 0, 1, 13]
+    q = r.standard_normal((B, Hq, d))
+    rho = r.standard_normal((B, Hq, d))
+    K = [r.standard_normal((Hkv, n, d)) * 2 for n in lens]
+    V = [r.standard_normal((Hkv, n, d)) for n in lens]
+    Kp = np.full((B, Hkv, cap, d), pad)
+    Vp = np.full((B, Hkv, cap, d), pad)
+    for b, n in enumerate(lens):
+        Kp[b, :, :n], Vp[b, :, :n] = K[b], V[b]
+    return q, rho, K, V, Kp, Vp, lens, Hkv
+
+
+def pin_decode_heads_equals_decode():
+    """decode_heads (the checker of sampled output rows) returns, for every
+    listed (b, h) pair in any order and with repeats, exactly row (b, h) of
+    decode(): on a ragged GQA batch with an empty and a one-key sequence, from
+    per-sequence arrays and from a NaN-padded cache (a read past a length would
+    give NaN)."""
+    q, rho, K, V, Kp, Vp, lens, Hkv = _ragged_gqa_case(12)
+    B, Hq = q.shape[:2]
+    pairs = [(b, h) for b in range(B) for h in range(Hq)]
+    order = _rng(13).permutation(len(pairs))
+    pairs = [pairs[i] for i in order] + [(3, 5), (0, 1), (3, 5)]
+    for Kc, Vc in ((K, V), (Kp, Vp)):
+        full = oracle.decode(q, rho, Kc, Vc, lens, Hkv)
+        got = oracle.decode_heads(q, rho, Kc, Vc, lens, Hkv, pairs)
+        assert np.isfinite(got).all()
+        np.testing.assert_array_equal(got, np.stack([full[b, h] for b, h in pairs]))
+    assert oracle.decode_heads(q, rho, K, V, lens, Hkv, []).shape == (0, q.shape[2])
+
+
+def pin_length_clamp():
+    """A length above the cache's rows counts as all of them and a negative one
+    as 0 (zero output), for decode and decode_heads alike; checked against
+    decode_head on explicitly sliced rows."""
+    q, rho, K, V, Kp, Vp, lens, Hkv = _ragged_gqa_case(14, pad=0.5)
+    Kp[2, :, :], Vp[2, :, :] = Kp[3, :, :], Vp[3, :, :]   # sequence 2: all 16 rows valid
+    lens2 = [-3, 0, 100, 13]
+    Hq = q.shape[1]
+    G = Hq // Hkv
+    full = oracle.decode(q, rho, Kp, Vp, lens2, Hkv)
+    rows = oracle.decode_heads(q, rho, Kp, Vp, lens2, Hkv, [(0, 4), (2, 5)])
+    assert np.all(full[0] == 0.0) and np.all(full[1] == 0.0) and np.all(rows[0] == 0.0)
+    for h in range(Hq):
+        ref = oracle.decode_head(q[2, h], rho[2, h], Kp[2, h // G, :16], Vp[2, h // G, :16])
+        np.testing.assert_allclose(full[2, h], ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(rows[1], full[2, 5], rtol=0, atol=0)
+
+
 ALL_PINS = [pin_golden_decode, pin_golden_gqa, pin_golden_probe, pin_probe_bruteforce,
             pin_wr_zero_is_softmax, pin_single_pass_identity, pin_local_linear_lstsq,
-            pin_closed_forms, pin_invariances, pin_bruteforce, pin_gqa_equals_mha]
+            pin_closed_forms, pin_invariances, pin_bruteforce, pin_gqa_equals_mha,
+            pin_decode_heads_equals_decode, pin_length_clamp]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -319,7 +375,34 @@ def _mut_probe_layout(W_R, x, Hq, d):
     return (X @ W.T).reshape(X.shape[0], d, Hq).transpose(0, 2, 1)
 
 
+def _mut_heads_pair_length(q, rho, K_parts, V_parts, seq_lens, Hkv, pairs):
+    """decode_heads taking the length of the i-th sequence for the i-th pair."""
+    Hq = q.shape[1]
+    res = []
+    for i, (b, h) in enumerate(pairs):
+        n = int(seq_lens[i % len(seq_lens)])
+        Kb, Vb = po._seq_kv(K_parts, V_parts, b, po.kv_head_of(h, Hq, Hkv), n)
+        res.append(po.decode_head(q[b, h], rho[b, h], Kb, Vb))
+    return np.stack(res) if res else np.zeros((0, q.shape[2]))
+
+
+def _mut_heads_no_kv_map(q, rho, K_parts, V_parts, seq_lens, Hkv, pairs):
+    """decode_heads reading KV head h instead of kv_head_of(h)."""
+    res = []
+    for b, h in pairs:
+        Kb, Vb = po._seq_kv(K_parts, V_parts, b, h % Hkv, int(seq_lens[b]))
+        res.append(po.decode_head(q[b, h], rho[b, h], Kb, Vb))
+    return np.stack(res) if res else np.zeros((0, q.shape[2]))
+
+
+def _mut_unclamped_rows(K_parts, V_parts, b, g, n):
+    return K_parts[b][g][:n], V_parts[b][g][:n]
+
+
 MUTANTS = {
+    "heads_length_of_pair_index": ("decode_heads", _mut_heads_pair_length),
+    "heads_without_kv_head_map": ("decode_heads", _mut_heads_no_kv_map),
+    "unclamped_length": ("_seq_kv", _mut_unclamped_rows),
     "transposed_covariance": ("kv_covariance", _mut_transposed_cov),
     "bessel_factor": ("kv_covariance", _mut_bessel),
     "raw_second_moment": ("kv_covariance", _mut_raw_second_moment),
@@ -342,6 +425,6 @@ def test_planted_mistakes(name, monkeypatch):
     for pin in ALL_PINS:
         try:
             pin()
-        except (AssertionError, np.linalg.LinAlgError, ValueError):
+        except (AssertionError, np.linalg.LinAlgError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"
