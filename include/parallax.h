@@ -23,10 +23,22 @@
  *   returns a non-zero parallax_status, enqueues nothing and leaves a message
  *   in parallax_last_error(). No C++ exception crosses this ABI.
  * - All tensors are dense, row-major (last index fastest), 16-byte aligned.
- * - dtype selects the storage type (see parallax_dtype). rho is always fp32
- *   and all accumulation is fp32.
- * - Calls are thread-safe; calls that share output buffers must be ordered by
- *   the caller.
+ * - dtype selects the storage type (see parallax_dtype). rho is passed as
+ *   fp32 and all accumulation is fp32. Precision of rho inside the kernels:
+ *   PARALLAX_F32 uses rho as given. The bf16 dtypes run on the matrix cores,
+ *   which carry each component of rho as two bf16 terms, hi = bf16(rho) and
+ *   lo = bf16(rho - hi) (round to nearest even): |rho_i - (hi_i + lo_i)| <=
+ *   2^-16 |rho_i|, about 16 significant bits. The probes p_j = k_j . rho then
+ *   differ from their fp32 value by at most 2^-16 sum_i |k_ji rho_i|, and the
+ *   output by at most 2^-16 sum_j w_j (sum_i |k_ji rho_i|) |v_j - vbar| per
+ *   component (w: the softmax weights), beyond fp32 rounding. This is far
+ *   below the bf16 output's rounding; it matters only when rho is an exact
+ *   solve (local linear attention) read through an fp32 output.
+ * - Calls may be made from several threads at once: options are atomic, the
+ *   workspace cache and the profiling records are locked, and the error
+ *   message is per thread. Calls that share output buffers, or that run on
+ *   one stream (they share that stream's workspace), must be ordered by the
+ *   caller, as stream order does.
  */
 #ifndef PARALLAX_H_
 #define PARALLAX_H_
@@ -93,16 +105,22 @@ int parallax_probe(const void* W_R, const void* x, float* rho,
  *
  * Requires B, Hq, Hkv, max_ctx >= 1, Hq % Hkv == 0, d in {64, 128}. A sequence
  * with seq_lens[b] == 0 gets out = 0 (a convention). seq_lens[b] > max_ctx is
- * clamped to max_ctx on the device (memory safety; a caller error).
+ * clamped to max_ctx and seq_lens[b] < 0 to 0 on the device (memory safety; a
+ * caller error).
  *
  * Long sequences are split into chunks processed in parallel and a second
  * kernel merges the chunks' states by their running maxima (sequences that fit
  * in one chunk are finished by the first kernel). The chunk states live in a
  * workspace the library owns, cached per (device, stream) and kept until the
- * process ends; it grows stream-ordered on `stream` (hipMallocAsync, old
- * buffer hipFreeAsync'd). Growing is refused (PARALLAX_ERR_NO_MEMORY) while
+ * process ends; it grows stream-ordered on `stream` (hipMallocAsync, at least
+ * doubling; the old buffer is kept). Growing is refused (PARALLAX_ERR_NO_MEMORY) while
  * `stream` is being captured into a graph: make one call of the largest shape
- * on that stream before capturing. The cache is keyed by the stream handle: a
+ * on that stream before capturing. A graph captured on a stream uses that
+ * stream's workspace at the address it had during capture (a buffer the
+ * workspace grows out of is kept, never freed, so the address stays valid):
+ * replays of such a graph, eager calls on the capture stream and other graphs
+ * captured on it all write the same partial states, so they must not run
+ * concurrently with each other. The cache is keyed by the stream handle: a
  * stream with library work still pending must be synchronised before it is
  * destroyed, since a stream created afterwards may receive the same handle and
  * would share the workspace.

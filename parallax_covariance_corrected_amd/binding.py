@@ -82,40 +82,89 @@ def _ptr(t: torch.Tensor) -> int:
     return t.data_ptr()
 
 
-def _stream() -> int:
-    return torch.cuda.current_stream().cuda_stream
-
-
 def _dtype_code(t: torch.dtype, out_dtype: torch.dtype) -> int:
     if t == torch.float32:
         if out_dtype != torch.float32:
             raise ValueError("fp32 inputs produce an fp32 output")
         return F32
     if t == torch.bfloat16:
+        if out_dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError(f"out must be bfloat16 or float32, got {out_dtype}")
         return BF16 if out_dtype == torch.bfloat16 else BF16_F32OUT
     raise ValueError(f"unsupported dtype {t}")
 
 
-def _need(t: torch.Tensor, name: str):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+def _shape(t: torch.Tensor, name: str, shape, dtype=None):
+    """Raise ValueError unless t has exactly this shape (and dtype)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _rank(t: torch.Tensor, name: str, n: int):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+
+
+def _stream_of(tensors) -> int:
+    """Check that every tensor is a contiguous tensor on one GPU and return the
+    HIP stream handle of that GPU's current stream (the library launches on the
+    calling thread's current device, so the call runs under that device)."""
+    dev = None
+    for t, name in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+    if dev.index is not None and dev.index != torch.cuda.current_device():
+        raise ValueError(f"the tensors are on {dev}; make it the current device "
+                         "(torch.cuda.device) before the call")
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _out(out, shape, dtype, like: torch.Tensor) -> torch.Tensor:
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    return out
 
 
 def probe(W_R: torch.Tensor, x: torch.Tensor, Hq: int, d: int,
           out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """rho[B, Hq, d] (fp32) = x[B, d_model] . W_R[Hq*d, d_model]^T on the current stream."""
-    _need(W_R, "W_R"); _need(x, "x")
+    _rank(x, "x", 2)
     B, d_model = x.shape
-    if out is None:
-        out = torch.empty((B, Hq, d), dtype=torch.float32, device=x.device)
-    _need(out, "rho")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    _shape(W_R, "W_R", (Hq * d, d_model), x.dtype)
+    if out is not None:
+        _shape(out, "rho", (B, Hq, d), torch.float32)
+    st = _stream_of([(W_R, "W_R"), (x, "x"), (out, "rho")])
+    out = _out(out, (B, Hq, d), torch.float32, x)
     code = F32 if x.dtype == torch.float32 else BF16
-    if W_R.dtype != x.dtype:
-        raise ValueError("W_R and x must share a dtype")
-    _check(lib().parallax_probe(_ptr(W_R), _ptr(x), _ptr(out), B, Hq, d, d_model, code, _stream()))
+    _check(lib().parallax_probe(_ptr(W_R), _ptr(x), _ptr(out), B, Hq, d, d_model, code, st))
     return out
+
+
+def _decode_shapes(q, k_cache, v_cache, seq_lens, rho=None):
+    """Sizes of a decode call from q [B, Hq, d] and k_cache [B, Hkv, max_ctx, d];
+    every other tensor is checked against them."""
+    _rank(q, "q", 3)
+    _rank(k_cache, "k_cache", 4)
+    B, Hq, d = q.shape
+    Hkv, max_ctx = k_cache.shape[1], k_cache.shape[2]
+    _shape(k_cache, "k_cache", (B, Hkv, max_ctx, d), q.dtype)
+    _shape(v_cache, "v_cache", (B, Hkv, max_ctx, d), q.dtype)
+    _shape(seq_lens, "seq_lens", (B,), torch.int32)
+    if rho is not None:
+        _shape(rho, "rho", (B, Hq, d), torch.float32)
+    return B, Hq, Hkv, d, max_ctx
 
 
 def decode(q: torch.Tensor, rho: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -123,22 +172,18 @@ def decode(q: torch.Tensor, rho: torch.Tensor, k_cache: torch.Tensor, v_cache: t
            out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     """Parallax decode: out[B, Hq, d] from q[B, Hq, d], rho[B, Hq, d] (fp32),
     k_cache/v_cache[B, Hkv, max_ctx, d], seq_lens[B] (int32), on the current stream."""
-    for t, nm in ((q, "q"), (rho, "rho"), (k_cache, "k_cache"), (v_cache, "v_cache"),
-                  (seq_lens, "seq_lens")):
-        _need(t, nm)
-    B, Hq, d = q.shape
-    _, Hkv, max_ctx, _ = k_cache.shape
-    if rho.dtype != torch.float32 or seq_lens.dtype != torch.int32:
-        raise ValueError("rho must be fp32 and seq_lens int32")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("q, k_cache and v_cache must share a dtype")
-    if out is None:
-        out = torch.empty((B, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out, "out")
-    code = _dtype_code(q.dtype, out.dtype)
+    if rho is None:
+        raise ValueError("rho is required (softmax_decode runs without the correction)")
+    B, Hq, Hkv, d, max_ctx = _decode_shapes(q, k_cache, v_cache, seq_lens, rho)
+    odt = out.dtype if out is not None else (out_dtype or q.dtype)
+    code = _dtype_code(q.dtype, odt)
+    if out is not None:
+        _shape(out, "out", (B, Hq, d))
+    st = _stream_of([(q, "q"), (rho, "rho"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                     (seq_lens, "seq_lens"), (out, "out")])
+    out = _out(out, (B, Hq, d), odt, q)
     _check(lib().parallax_decode(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache),
-                                 _ptr(seq_lens), _ptr(out), B, Hq, Hkv, d, max_ctx, code,
-                                 _stream()))
+                                 _ptr(seq_lens), _ptr(out), B, Hq, Hkv, d, max_ctx, code, st))
     return out
 
 
@@ -150,25 +195,21 @@ def probe_decode(W_R: torch.Tensor, x: torch.Tensor, q: torch.Tensor, k_cache: t
     out[B, Hq, d] from W_R[Hq*d, d_model], x[B, d_model], q[B, Hq, d],
     k_cache/v_cache[B, Hkv, max_ctx, d] and seq_lens[B] (int32), on the
     current stream."""
-    for t, nm in ((W_R, "W_R"), (x, "x"), (q, "q"), (k_cache, "k_cache"),
-                  (v_cache, "v_cache"), (seq_lens, "seq_lens")):
-        _need(t, nm)
-    B, Hq, d = q.shape
-    _, Hkv, max_ctx, _ = k_cache.shape
+    B, Hq, Hkv, d, max_ctx = _decode_shapes(q, k_cache, v_cache, seq_lens)
+    _rank(x, "x", 2)
     d_model = x.shape[1]
-    if seq_lens.dtype != torch.int32:
-        raise ValueError("seq_lens must be int32")
-    if any(t.dtype != q.dtype for t in (W_R, x, k_cache, v_cache)):
-        raise ValueError("W_R, x, q, k_cache and v_cache must share a dtype")
-    if tuple(W_R.shape) != (Hq * d, d_model) or x.shape[0] != B:
-        raise ValueError("W_R must be [Hq*d, d_model] and x [B, d_model]")
-    if out is None:
-        out = torch.empty((B, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out, "out")
-    code = _dtype_code(q.dtype, out.dtype)
+    _shape(x, "x", (B, d_model), q.dtype)
+    _shape(W_R, "W_R", (Hq * d, d_model), q.dtype)
+    odt = out.dtype if out is not None else (out_dtype or q.dtype)
+    code = _dtype_code(q.dtype, odt)
+    if out is not None:
+        _shape(out, "out", (B, Hq, d))
+    st = _stream_of([(W_R, "W_R"), (x, "x"), (q, "q"), (k_cache, "k_cache"),
+                     (v_cache, "v_cache"), (seq_lens, "seq_lens"), (out, "out")])
+    out = _out(out, (B, Hq, d), odt, q)
     _check(lib().parallax_probe_decode(_ptr(W_R), _ptr(x), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                        _ptr(seq_lens), _ptr(out), B, Hq, Hkv, d, d_model, max_ctx,
-                                       code, _stream()))
+                                       code, st))
     return out
 
 
@@ -177,20 +218,16 @@ def softmax_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     """Plain softmax attention decode (the same kernel without the correction
     branch): out[B, Hq, d] from q, k_cache/v_cache [B, Hkv, max_ctx, d], seq_lens."""
-    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
-        _need(t, nm)
-    B, Hq, d = q.shape
-    _, Hkv, max_ctx, _ = k_cache.shape
-    if seq_lens.dtype != torch.int32:
-        raise ValueError("seq_lens must be int32")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("q, k_cache and v_cache must share a dtype")
-    if out is None:
-        out = torch.empty((B, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out, "out")
-    code = _dtype_code(q.dtype, out.dtype)
+    B, Hq, Hkv, d, max_ctx = _decode_shapes(q, k_cache, v_cache, seq_lens)
+    odt = out.dtype if out is not None else (out_dtype or q.dtype)
+    code = _dtype_code(q.dtype, odt)
+    if out is not None:
+        _shape(out, "out", (B, Hq, d))
+    st = _stream_of([(q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                     (seq_lens, "seq_lens"), (out, "out")])
+    out = _out(out, (B, Hq, d), odt, q)
     _check(lib().parallax_softmax_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
-                                         _ptr(out), B, Hq, Hkv, d, max_ctx, code, _stream()))
+                                         _ptr(out), B, Hq, Hkv, d, max_ctx, code, st))
     return out
 
 
@@ -202,43 +239,42 @@ def prefill(q: torch.Tensor, rho: Optional[torch.Tensor], k_cache: torch.Tensor,
     rho [B, T, Hq, d] (fp32) and a cache [B, Hkv, max_ctx, d] holding each
     sequence's prefix_lens[b] cached tokens followed by its T new ones.
     rho=None runs plain softmax attention (parallax_softmax_prefill)."""
-    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _need(t, nm)
+    _rank(q, "q", 4)
+    _rank(k_cache, "k_cache", 4)
     B, T, Hq, d = q.shape
-    _, Hkv, max_ctx, _ = k_cache.shape
+    Hkv, max_ctx = k_cache.shape[1], k_cache.shape[2]
+    _shape(k_cache, "k_cache", (B, Hkv, max_ctx, d), q.dtype)
+    _shape(v_cache, "v_cache", (B, Hkv, max_ctx, d), q.dtype)
     if rho is not None:
-        _need(rho, "rho")
-        if rho.dtype != torch.float32 or tuple(rho.shape) != (B, T, Hq, d):
-            raise ValueError("rho must be float32 [B, T, Hq, d]")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("q, k_cache and v_cache must share a dtype")
-    pp = None
+        _shape(rho, "rho", (B, T, Hq, d), torch.float32)
     if prefix_lens is not None:
-        _need(prefix_lens, "prefix_lens")
-        if prefix_lens.dtype != torch.int32:
-            raise ValueError("prefix_lens must be int32")
-        pp = _ptr(prefix_lens)
-    if out is None:
-        out = torch.empty((B, T, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out, "out")
-    code = _dtype_code(q.dtype, out.dtype)
+        _shape(prefix_lens, "prefix_lens", (B,), torch.int32)
+    odt = out.dtype if out is not None else (out_dtype or q.dtype)
+    code = _dtype_code(q.dtype, odt)
+    if out is not None:
+        _shape(out, "out", (B, T, Hq, d))
+    st = _stream_of([(q, "q"), (rho, "rho"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                     (prefix_lens, "prefix_lens"), (out, "out")])
+    out = _out(out, (B, T, Hq, d), odt, q)
+    pp = _ptr(prefix_lens) if prefix_lens is not None else None
     if rho is None:
         _check(lib().parallax_softmax_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), pp, _ptr(out),
-                                              B, T, Hq, Hkv, d, max_ctx, code, _stream()))
+                                              B, T, Hq, Hkv, d, max_ctx, code, st))
     else:
         _check(lib().parallax_prefill(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), pp,
-                                      _ptr(out), B, T, Hq, Hkv, d, max_ctx, code, _stream()))
+                                      _ptr(out), B, T, Hq, Hkv, d, max_ctx, code, st))
     return out
 
 
 def read_bandwidth(buf: torch.Tensor, sink: torch.Tensor):
     """Measurement hook: stream `buf` (contiguous, device, size a multiple of
     1 MiB) once with the decode's load shape; time it with options(profile=1)
-    and profile_read(KERNEL_READ)."""
-    _need(buf, "buf")
-    _need(sink, "sink")
+    and profile_read(KERNEL_READ). sink: at least 4 bytes the kernel may write."""
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    st = _stream_of([(buf, "buf"), (sink, "sink")])
     nbytes = buf.numel() * buf.element_size()
-    _check(lib().parallax_read_bandwidth(_ptr(buf), nbytes, _ptr(sink), _stream()))
+    _check(lib().parallax_read_bandwidth(_ptr(buf), nbytes, _ptr(sink), st))
 
 
 def decode_plan(B: int, Hq: int, Hkv: int, d: int, max_ctx: int, dtype: int = BF16):

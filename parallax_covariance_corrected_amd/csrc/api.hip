@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <iterator>
 #include <map>
 #include <mutex>
@@ -35,12 +36,14 @@ int hip_fail(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // ---------------------------------------------------------------- options
-int g_opt_chunk = 0;
-int g_opt_kernel = 0;
-int g_opt_profile = 0;
-int g_opt_items = 0;
-int g_opt_order = 0;
-int g_opt_fuse = 0;
+// Process-wide; atomics so that a call on one thread may overlap
+// parallax_set_option on another (the call then sees the old or the new value).
+std::atomic<int> g_opt_chunk{0};
+std::atomic<int> g_opt_kernel{0};
+std::atomic<int> g_opt_profile{0};
+std::atomic<int> g_opt_items{0};
+std::atomic<int> g_opt_order{0};
+std::atomic<int> g_opt_fuse{0};
 
 // ---------------------------------------------------------------- profiling
 // Start/stop events are handed to hipExtLaunchKernel, which stamps them from
@@ -93,15 +96,18 @@ void profile_record(int kind, parallax::LaunchEvents ev, bool launched) {
 // ---------------------------------------------------------------- workspace
 // Split-K partial states, cached per (device, stream): calls on one stream are
 // ordered, so they can share one buffer; calls on different streams never do.
-// A buffer only grows; growing is stream-ordered (allocate, then free the old
-// one on the same stream) and is refused while the stream is being captured
-// into a graph.
+// A buffer only grows (at least doubling, so retired buffers add up to less
+// than the current one); growing is stream-ordered and is refused while the
+// stream is being captured into a graph. A retired buffer is never freed: a
+// graph captured earlier on the stream still holds its address, and a replay
+// of that graph must not write freed memory.
 struct Workspace {
   void* base = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<void*> g_ws_retired;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -120,15 +126,11 @@ int get_workspace(hipStream_t stream, size_t bytes, void** base) {
                   "the split-K workspace of this stream must grow, which cannot happen during "
                   "graph capture: run one call of this size on the stream before capturing");
     Workspace nw;
-    nw.bytes = round_up(std::max(bytes, w.bytes), 1 << 20);
+    nw.bytes = round_up(std::max(bytes, 2 * w.bytes), 1 << 20);
     e = hipMallocAsync(&nw.base, nw.bytes, stream);
     if (e != hipSuccess || !nw.base) return fail(PARALLAX_ERR_NO_MEMORY, "workspace allocation failed");
-    void* old = w.base;
-    w = nw;   // the new buffer is in use from here on, whatever happens to the old one
-    if (old) {
-      e = hipFreeAsync(old, stream);
-      if (e != hipSuccess) return hip_fail(e, "hipFreeAsync");
-    }
+    if (w.base) g_ws_retired.push_back(w.base);
+    w = nw;
   }
   *base = w.base;
   return PARALLAX_OK;

@@ -199,3 +199,104 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(pb, "LIB_PATH", str(tmp_path / "libparallax.so"))
     with pytest.raises(RuntimeError, match="not built"):
         pb.lib()
+
+
+# ---------------------------------------------------------------- Python binding checks
+# The C ABI sees only pointers, so the binding checks every tensor's shape,
+# dtype and device against the sizes it passes; a mismatch raises ValueError
+# before the library is touched (here: CPU tensors and a library that fails the
+# test if it is called).
+@pytest.fixture
+def no_lib(monkeypatch):
+    def _fail():
+        raise AssertionError("the library was called")
+    monkeypatch.setattr(pb, "lib", _fail)
+
+
+def _dec_args(B=2, Hq=4, Hkv=2, d=64, ctx=32, dt=None):
+    import torch
+    dt = dt or torch.bfloat16
+    return dict(q=torch.zeros(B, Hq, d, dtype=dt), rho=torch.zeros(B, Hq, d),
+                k_cache=torch.zeros(B, Hkv, ctx, d, dtype=dt),
+                v_cache=torch.zeros(B, Hkv, ctx, d, dtype=dt),
+                seq_lens=torch.zeros(B, dtype=torch.int32))
+
+
+def _bad_decode_cases():
+    import torch
+    return [
+        ("rho", lambda a: a.update(rho=torch.zeros(2, 4, 32)), "rho must have shape"),
+        ("rho", lambda a: a.update(rho=torch.zeros(2, 4, 64, dtype=torch.bfloat16)), "rho must be"),
+        ("v_cache", lambda a: a.update(v_cache=torch.zeros(2, 2, 16, 64, dtype=torch.bfloat16)),
+         "v_cache must have shape"),
+        ("k_cache", lambda a: a.update(k_cache=torch.zeros(3, 2, 32, 64, dtype=torch.bfloat16),
+                                       v_cache=torch.zeros(3, 2, 32, 64, dtype=torch.bfloat16)),
+         "k_cache must have shape"),
+        ("k_cache", lambda a: a.update(k_cache=torch.zeros(2, 2, 32, 128, dtype=torch.bfloat16)),
+         "k_cache must have shape"),
+        ("k_cache", lambda a: a.update(k_cache=torch.zeros(2, 2, 32, 64)), "k_cache must be"),
+        ("seq_lens", lambda a: a.update(seq_lens=torch.zeros(3, dtype=torch.int32)),
+         "seq_lens must have shape"),
+        ("seq_lens", lambda a: a.update(seq_lens=torch.zeros(2, dtype=torch.int64)),
+         "seq_lens must be"),
+        ("out", lambda a: a.update(out=torch.zeros(2, 4, 32, dtype=torch.bfloat16)),
+         "out must have shape"),
+        ("out", lambda a: a.update(out=torch.zeros(2, 4, 64, dtype=torch.float16)),
+         "out must be bfloat16 or float32"),
+    ]
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_binding_decode_rejects_mismatched_tensors(no_lib, i):
+    name, mutate, msg = _bad_decode_cases()[i]
+    a = _dec_args()
+    mutate(a)
+    with pytest.raises(ValueError, match=msg):
+        pb.decode(**a)
+    a.pop("rho")
+    if name != "rho":
+        with pytest.raises(ValueError, match=msg):
+            pb.softmax_decode(**a)
+
+
+def test_binding_rejects_before_the_library(no_lib):
+    import torch
+    a = _dec_args()
+    with pytest.raises(ValueError, match="device tensor"):   # right shapes, host memory
+        pb.decode(**a)
+    with pytest.raises(ValueError, match="rho is required"):
+        pb.decode(**{**a, "rho": None})
+    f = _dec_args(dt=torch.float32)
+    with pytest.raises(ValueError, match="fp32 inputs produce an fp32 output"):
+        pb.decode(**f, out=torch.zeros(2, 4, 64, dtype=torch.bfloat16))
+    # probe: a bf16 rho buffer would be written at 4 bytes per element
+    W, x = torch.zeros(4 * 64, 128, dtype=torch.bfloat16), torch.zeros(2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="rho must be torch.float32"):
+        pb.probe(W, x, 4, 64, out=torch.zeros(2, 4, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="rho must have shape"):
+        pb.probe(W, x, 4, 64, out=torch.zeros(2, 4, 32))
+    with pytest.raises(ValueError, match="W_R must have shape"):
+        pb.probe(W[:, :64], x, 4, 64)
+    with pytest.raises(ValueError, match="W_R must be"):
+        pb.probe(W.float(), x, 4, 64)
+    # probe_decode: x and W_R against q
+    a.pop("rho")
+    with pytest.raises(ValueError, match="x must have shape"):
+        pb.probe_decode(W, torch.zeros(3, 128, dtype=torch.bfloat16), **a)
+    with pytest.raises(ValueError, match="W_R must have shape"):
+        pb.probe_decode(torch.zeros(4 * 32, 128, dtype=torch.bfloat16), x, **a)
+    with pytest.raises(ValueError, match="seq_lens must have shape"):
+        pb.probe_decode(W, x, **{**a, "seq_lens": torch.zeros(1, dtype=torch.int32)})
+    # prefill: q [B, T, Hq, d]
+    q = torch.zeros(2, 5, 4, 64, dtype=torch.bfloat16)
+    K = torch.zeros(2, 2, 32, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="rho must have shape"):
+        pb.prefill(q, torch.zeros(2, 4, 4, 64), K, K)
+    with pytest.raises(ValueError, match="prefix_lens must have shape"):
+        pb.prefill(q, None, K, K, prefix_lens=torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="out must have shape"):
+        pb.prefill(q, None, K, K, out=torch.zeros(2, 5, 4, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="device tensor"):
+        pb.prefill(q, None, K, K)
+    with pytest.raises(ValueError, match="sink must hold"):
+        pb.read_bandwidth(torch.zeros(1 << 20, dtype=torch.uint8), torch.zeros(0, dtype=torch.int32))

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from oracle import lla_oracle as lla
 from parallax_covariance_corrected_amd import binding as pb
 from parallax_covariance_corrected_amd.workloads import WORKLOADS, make_inputs
@@ -49,5 +50,22 @@ def test_decode_with_solved_probe_is_exact_lla(d, chunk):
         f"max-abs {max_abs(to64(o32), want):.2e}, bf16 rel {rel_l2(to64(obf), want):.2e}")
     assert e_model <= 2e-6
     assert e_lla <= 5e-5
+    # The bound the boundary documents for the 16-bit probe, computed here in
+    # fp64 from the oracle's weights: per output component,
+    # 2^-16 sum_j w_j (sum_i |k_ji rho_i|) |v_j - vbar| (plus fp32 rounding of
+    # rho itself and of the kernel's sums), against the exact LLA output.
+    G = wl.Hq // wl.Hkv
+    got = to64(o32)
+    scale = np.abs(want).max()
+    for b, n in enumerate(s.seq_lens.tolist()):
+        for h in range(wl.Hq):
+            Kb = s.K[b][h // G].double().numpy()
+            Vb = s.V[b][h // G].double().numpy()
+            w = oracle.softmax_weights(q64[b, h], Kb)
+            vbar = w @ Vb
+            kr = np.abs(Kb) @ np.abs(rho[b, h])
+            bound = (2.0 ** -16 + 2.0 ** -24) * ((w * kr) @ np.abs(Vb - vbar))
+            err = np.abs(got[b, h] - want[b, h])
+            assert np.all(err <= bound + 2e-6 * scale), (b, h, float((err - bound).max()))
     assert max_abs(to64(o32), want) <= 1e-3
     assert rel_l2(to64(obf), want) <= BF16_REL_L2
