@@ -9,10 +9,12 @@ several independently seeded input sets are rotated so that every step reads
 its K/V cold (their total exceeds the last-level cache).
 
 Output: one JSON line (metric, value = decode tokens/s, ms_per_step, roofline
-of the dominant kernel, CPU oracle baseline, ...).
+of the dominant kernel, CPU oracle baseline, ...), with a compact record per
+other workload under "configs" (step and per-kernel times, algorithmic bytes,
+fraction of peak, launch plan).
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload 2]
-                    [--sets 3] [--no-cpu-baseline] [--sweep] [--fusion-sweep]
+                    [--sets 3] [--no-cpu-baseline] [--no-configs] [--sweep] [--fusion-sweep]
                     [--copy-calibration]
 """
 from __future__ import annotations
@@ -231,6 +233,69 @@ def correction_ratio(pb, d):
     return round(float((par - soft).norm() / par.norm()), 4)
 
 
+def run_config(args, wl_id: int, reps: int):
+    """One of the other workloads, measured like the main line but compactly:
+    whole steps (parallax_probe_decode) timed back to back, then the same steps
+    with per-launch events for the probe, decode and merge kernels. x, W_R, q
+    and the lengths are the seeded host draws; K/V are drawn on the device
+    (same distribution), with enough rotated sets that at least 1 GiB of other
+    K/V streams between two uses of one set (every step reads cold)."""
+    import math
+    import torch
+    from parallax_covariance_corrected_amd import binding as pb
+    from parallax_covariance_corrected_amd.workloads import (WORKLOADS, algorithmic_bytes,
+                                                             device_cache, make_inputs)
+    wl = WORKLOADS[wl_id]
+    print(f"# bench: config {wl.name}", file=sys.stderr, flush=True)
+    es = 2 if wl.dtype == "bf16" else 4
+    first = make_inputs(wl, 0, with_kv=False)
+    kv_set = 2 * first.total_tokens() * wl.Hkv * wl.d * es
+    nsets = max(2, min(12, 1 + math.ceil((1 << 30) / max(kv_set, 1))))
+    sets, tokens = [], []
+    for seed in range(nsets):
+        h = first if seed == 0 else make_inputs(wl, seed, with_kv=False)
+        K, V = device_cache(wl, 1000 + seed)
+        sets.append(dict(W_R=h.W_R.cuda(), x=h.x.cuda(), q=h.q.cuda(), seq_lens=h.seq_lens.cuda(),
+                         K=K, V=V, out=torch.empty((wl.B, wl.Hq, wl.d), dtype=h.q.dtype,
+                                                   device="cuda")))
+        tokens.append(h.total_tokens())
+    torch.cuda.synchronize()
+    code = pb.BF16 if wl.dtype == "bf16" else pb.F32
+    chunk, splits, kernel = pb.decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.capacity, code)
+    fused = pb.probe_decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.d_model, wl.capacity, code)
+    step_us = timed_steps(lambda i: step(pb, wl, sets[i % nsets]), reps, warm=max(args.warmup, 3))
+    pb.profile_reset()
+    with pb.options(profile=1):
+        for i in range(reps):
+            step(pb, wl, sets[i % nsets])
+        torch.cuda.synchronize()
+        per = {}
+        for name, k in (("probe", pb.KERNEL_PROBE), ("decode", pb.KERNEL_DECODE),
+                        ("merge", pb.KERNEL_MERGE)):
+            ms, n = pb.profile_read(k)
+            per[name] = ms / n * 1e3 if n else 0.0
+    ab = [algorithmic_bytes(wl, t) for t in tokens]
+    dec_bytes = sum(a["decode_read"] for a in ab) / len(ab)
+    step_bytes = sum(a["total"] for a in ab) / len(ab) + wl.Hq * wl.d * wl.d_model * es
+
+    def frac(us):
+        return round(dec_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4) if us > 0 else None
+    rec = {"workload": wl.name, "tokens_per_s": round(wl.B / (step_us * 1e-6), 1),
+           "step_us": round(step_us, 3), "decode_kernel_us": round(per["decode"], 3),
+           "merge_us": round(per["merge"], 3), "probe_us": round(per["probe"], 3),
+           "decode_bytes_per_launch": int(dec_bytes),
+           "frac_decode_kernel": frac(per["decode"]),
+           "frac_decode_call": frac(per["decode"] + per["merge"]),
+           "pct_peak_step": round(100 * step_bytes / (step_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+           "mean_tokens_per_set": round(sum(tokens) / len(tokens), 1),
+           "kv_sets_rotated": nsets, "reps": reps,
+           "plan": {"chunk": chunk, "splits": splits, "kernel": kernel,
+                    "probe": "fused" if fused else "separate"}}
+    del sets
+    torch.cuda.empty_cache()
+    return rec
+
+
 def run_workload(args, wl_id: int, emit: bool = True):
     import torch
     from parallax_covariance_corrected_amd import binding as pb
@@ -278,10 +343,12 @@ def run_workload(args, wl_id: int, emit: bool = True):
 
     ms_step = total_ms / args.steps
     # algorithmic bytes, averaged over the rotated sets
+    es = 2 if wl.dtype == "bf16" else 4
     ab = [algorithmic_bytes(wl, t) for t in tokens]
-    step_bytes = sum(a["total"] for a in ab) / len(ab) + wl.Hq * wl.d * wl.d_model * 2
+    step_bytes = sum(a["total"] for a in ab) / len(ab) + wl.Hq * wl.d * wl.d_model * es
     dec_bytes = sum(a["decode_read"] for a in ab) / len(ab)
     dec_avg_ms = dec_ms / max(dec_n, 1)
+    mrg_avg_ms = mrg_ms / mrg_n if mrg_n else 0.0
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
     traffic = measured_traffic(wl.name)
     rec = {
@@ -311,7 +378,10 @@ def run_workload(args, wl_id: int, emit: bool = True):
                                + (" (probe fused in)" if fused else " (split-K pass)"),
                      "bytes_per_launch": int(dec_bytes),
                      "avg_launch_us": round(dec_avg_ms * 1e3, 3),
-                     "merge_avg_us": round(mrg_ms / max(mrg_n, 1) * 1e3, 3),
+                     "merge_avg_us": round(mrg_avg_ms * 1e3, 3),
+                     # the decode call (split-K pass + merge launch) over the same bytes
+                     "frac_decode_call": round(dec_bytes / ((dec_avg_ms + mrg_avg_ms) * 1e-3)
+                                               / 1e9 / PEAK_HBM_GBS, 4),
                      "probe_avg_us": round(prb_ms / max(prb_n, 1) * 1e3, 3)},
         "cpu_baseline": None,
     }
@@ -326,6 +396,11 @@ def run_workload(args, wl_id: int, emit: bool = True):
     if args.cpu_baseline:
         print("# bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(sets_host[0])
+    if args.configs:
+        del dev_sets
+        torch.cuda.empty_cache()
+        rec["configs"] = {str(i): run_config(args, i, max(args.steps, 20))
+                          for i in sorted(WORKLOADS) if i != wl_id}
     if emit:
         print(json.dumps(rec), flush=True)
     return rec
@@ -584,6 +659,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the compact records of the other four workloads")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 256 MiB device-to-device 3 times (a kernel of known "

@@ -32,7 +32,7 @@ from typing import List, Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "InputSet", "make_inputs", "padded_cache",
+__all__ = ["Workload", "WORKLOADS", "InputSet", "make_inputs", "padded_cache", "device_cache",
            "algorithmic_bytes", "sweep_points"]
 
 
@@ -120,12 +120,15 @@ def draw_lengths(g: torch.Generator, B: int, lo: int, hi: int) -> torch.Tensor:
 
 
 def make_inputs(wl: Workload, seed: int = 0, *, wr_zero: bool = False,
-                lengths: Optional[List[int]] = None) -> InputSet:
+                lengths: Optional[List[int]] = None, with_kv: bool = True) -> InputSet:
     """Draw one input set in the fixed order documented in the module header.
 
     ``wr_zero`` replaces W_R by zeros after drawing it (so the rest of the
     stream is unchanged). ``lengths`` overrides the per-sequence lengths (the
     lengths draw is then skipped); each must lie in [0, capacity].
+    ``with_kv=False`` stops after the lengths (K and V are left empty): x, W_R,
+    q and the lengths are those of the full draw, for callers that fill the
+    cache themselves (the benchmark draws K/V on the device).
     """
     dt = torch_dtype(wl.dtype)
     g = torch.Generator("cpu").manual_seed(seed)
@@ -145,11 +148,27 @@ def make_inputs(wl: Workload, seed: int = 0, *, wr_zero: bool = False,
     else:
         seq = torch.full((wl.B,), wl.ctx, dtype=torch.int32)
     K, V = [], []
-    for b in range(wl.B):
+    for b in range(wl.B if with_kv else 0):
         n = int(seq[b])
         K.append(_normal(g, (wl.Hkv, n, wl.d), wl.k_scale, dt))
         V.append(_normal(g, (wl.Hkv, n, wl.d), 1.0, dt))
     return InputSet(wl, seed, x, W_R, q, seq, K, V)
+
+
+def device_cache(wl: Workload, seed: int, device="cuda"):
+    """K and V caches [B, Hkv, capacity, d] drawn directly in device memory
+    (normals from a device generator, keys scaled by k_scale, rounded to the
+    storage dtype): the same distribution as make_inputs, other values, every
+    row filled (rows past a sequence's length are never read). For timing
+    runs, where drawing gigabytes on the host would dominate."""
+    dt = torch_dtype(wl.dtype)
+    g = torch.Generator(device=device).manual_seed(seed)
+    shape = (wl.B, wl.Hkv, wl.capacity, wl.d)
+    K = torch.randn(shape, generator=g, device=device, dtype=dt)
+    if wl.k_scale != 1.0:
+        K.mul_(wl.k_scale)
+    V = torch.randn(shape, generator=g, device=device, dtype=dt)
+    return K, V
 
 
 @dataclass
