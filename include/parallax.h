@@ -175,6 +175,33 @@ int parallax_probe_decode(const void* W_R, const void* x, const void* q, const v
                           hipStream_t stream);
 
 /*
+ * parallax_probe_decode_noalloc — parallax_probe_decode for callers that must
+ * not allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid allocation. Same arguments, plan,
+ * kernels and results as parallax_probe_decode (bit for bit); it never calls
+ * an allocator and records no profiling events.
+ *
+ * The probe's rho (separate-probe plan) and the split-K states live in a
+ * static device array of parallax_noalloc_scratch_bytes() bytes (64 MiB),
+ * one per device, held from the first call on that device until the process
+ * ends (that first call looks up the array's address; make it before any
+ * capture). A shape whose plan needs more — B*Hq*d*4 bytes for rho unless the
+ * probe is fused, plus B*Hq*splits*(16 + 8*d) bytes when sequences are split
+ * — returns PARALLAX_ERR_UNSUPPORTED with the sizes in the message (all five
+ * benchmark workloads fit). Nothing in the array needs clearing between calls.
+ * Every call on one device shares that device's array: calls that may overlap
+ * on one device (different streams, threads or graph replays) race on it and
+ * must be ordered by the caller. Errors otherwise as parallax_probe_decode.
+ */
+int parallax_probe_decode_noalloc(const void* W_R, const void* x, const void* q,
+                                  const void* k_cache, const void* v_cache, const int* seq_lens,
+                                  void* out, int B, int Hq, int Hkv, int d, int d_model,
+                                  int max_ctx, int dtype, hipStream_t stream);
+
+/* Size in bytes of the static scratch array of parallax_probe_decode_noalloc. */
+long long parallax_noalloc_scratch_bytes(void);
+
+/*
  * parallax_probe_decode_plan — writes 1 to *fused when parallax_probe_decode
  * would compute the probe inside the decode kernel for this shape, else 0.
  * Same shape checks as parallax_decode; d_model >= 1.

@@ -50,6 +50,10 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(i), ctypes.POINTER(i)]
         L.parallax_probe_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
         L.parallax_probe_decode_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i)]
+        L.parallax_probe_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp,
+                                                    i, i, i, i, i, i, i, vp]
+        L.parallax_noalloc_scratch_bytes.argtypes = []
+        L.parallax_noalloc_scratch_bytes.restype = ctypes.c_longlong
         L.parallax_set_option.argtypes = [i, i]
         L.parallax_get_option.argtypes = [i, ctypes.POINTER(i)]
         L.parallax_profile_read.argtypes = [i, ctypes.POINTER(ctypes.c_double),
@@ -58,6 +62,7 @@ def lib() -> ctypes.CDLL:
         for name in ("parallax_probe", "parallax_decode", "parallax_softmax_decode",
                      "parallax_prefill", "parallax_softmax_prefill", "parallax_read_bandwidth",
                      "parallax_decode_plan", "parallax_probe_decode", "parallax_probe_decode_plan",
+                     "parallax_probe_decode_noalloc",
                      "parallax_set_option", "parallax_get_option", "parallax_profile_read",
                      "parallax_profile_reset"):
             getattr(L, name).restype = i
@@ -70,7 +75,8 @@ def lib() -> ctypes.CDLL:
 def header_functions() -> list:
     """Names of the functions include/parallax.h declares."""
     txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(parallax_\w+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|long long|const char\*)\s+(parallax_\w+)\s*\(",
+                                 txt, re.M)))
 
 
 def _check(rc: int):
@@ -190,11 +196,13 @@ def decode(q: torch.Tensor, rho: torch.Tensor, k_cache: torch.Tensor, v_cache: t
 def probe_decode(W_R: torch.Tensor, x: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                  v_cache: torch.Tensor, seq_lens: torch.Tensor,
                  out: Optional[torch.Tensor] = None,
-                 out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+                 out_dtype: Optional[torch.dtype] = None, noalloc: bool = False) -> torch.Tensor:
     """One whole decode step (probe rho = W_R x, then the Parallax decode):
     out[B, Hq, d] from W_R[Hq*d, d_model], x[B, d_model], q[B, Hq, d],
     k_cache/v_cache[B, Hkv, max_ctx, d] and seq_lens[B] (int32), on the
-    current stream."""
+    current stream. noalloc=True calls parallax_probe_decode_noalloc (the
+    library's static scratch array instead of its workspace; pass `out` too
+    so that nothing is allocated on the Python side either)."""
     B, Hq, Hkv, d, max_ctx = _decode_shapes(q, k_cache, v_cache, seq_lens)
     _rank(x, "x", 2)
     d_model = x.shape[1]
@@ -207,9 +215,9 @@ def probe_decode(W_R: torch.Tensor, x: torch.Tensor, q: torch.Tensor, k_cache: t
     st = _stream_of([(W_R, "W_R"), (x, "x"), (q, "q"), (k_cache, "k_cache"),
                      (v_cache, "v_cache"), (seq_lens, "seq_lens"), (out, "out")])
     out = _out(out, (B, Hq, d), odt, q)
-    _check(lib().parallax_probe_decode(_ptr(W_R), _ptr(x), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                       _ptr(seq_lens), _ptr(out), B, Hq, Hkv, d, d_model, max_ctx,
-                                       code, st))
+    fn = lib().parallax_probe_decode_noalloc if noalloc else lib().parallax_probe_decode
+    _check(fn(_ptr(W_R), _ptr(x), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out),
+              B, Hq, Hkv, d, d_model, max_ctx, code, st))
     return out
 
 
@@ -292,6 +300,11 @@ def probe_decode_plan(B: int, Hq: int, Hkv: int, d: int, d_model: int, max_ctx: 
     _check(lib().parallax_probe_decode_plan(B, Hq, Hkv, d, d_model, max_ctx, dtype,
                                             ctypes.byref(f)))
     return bool(f.value)
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the static scratch array behind probe_decode(noalloc=True)."""
+    return int(lib().parallax_noalloc_scratch_bytes())
 
 
 def set_option(option: int, value: int):

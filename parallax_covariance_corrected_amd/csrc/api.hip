@@ -136,6 +136,36 @@ int get_workspace(hipStream_t stream, size_t bytes, void** base) {
   return PARALLAX_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+// parallax_probe_decode_noalloc keeps the probe's rho and the split states in
+// this file-scope device array instead of the per-stream workspace, so that it
+// never allocates. Each device holds its own copy (kScratchBytes) from the
+// library's first use on it until the process ends. In host code `scratch`
+// only names the symbol: its device address comes from hipGetSymbolAddress,
+// looked up once per device and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;   // device -> address of its scratch array
+
+int scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(PARALLAX_ERR_HIP, "hipGetSymbolAddress(scratch) gave null");
+    it = g_scratch_ptr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return PARALLAX_OK;
+}
+
 // ---------------------------------------------------------------- planning
 struct Plan {
   int chunk;
@@ -409,9 +439,20 @@ struct DecodeCall {
   void* front = nullptr;
 };
 
+// Workspace bytes of a planned decode call: `front` bytes for the caller
+// (rounded up to 256), then one (m, l, S) record and the A, P sums per
+// (sequence, query head, split) when there is more than one split.
+size_t decode_ws_bytes(const Plan& p, int B, int Hq, int d, size_t front_bytes) {
+  const size_t states = p.splits > 1 ? (size_t)B * Hq * p.splits : 0;
+  return round_up(front_bytes, 256) + states * sizeof(float4) + states * 2 * d * sizeof(float);
+}
+
+// use_scratch: take the workspace from the static scratch array (rejecting
+// plans that need more) instead of the per-stream workspace; no allocation.
 int setup_decode(const void* q, const float* rho, const void* k_cache, const void* v_cache,
                  const int* seq_lens, void* out, int B, int Hq, int Hkv, int d, int max_ctx,
-                 int dtype, size_t front_bytes, hipStream_t stream, DecodeCall& c) {
+                 int dtype, size_t front_bytes, hipStream_t stream, DecodeCall& c,
+                 bool use_scratch = false) {
   int rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
   if (rc != PARALLAX_OK) return rc;
   if (!q || !k_cache || !v_cache || !seq_lens || !out)
@@ -443,9 +484,18 @@ int setup_decode(const void* q, const float* rho, const void* k_cache, const voi
   const size_t front = round_up(front_bytes, 256);
   const size_t states = p.splits > 1 ? (size_t)B * Hq * p.splits : 0;
   if (front + states > 0) {
+    const size_t need = decode_ws_bytes(p, B, Hq, d, front_bytes);
     void* ws = nullptr;
-    rc = get_workspace(stream, front + states * sizeof(float4) + states * 2 * d * sizeof(float),
-                       &ws);
+    if (use_scratch) {
+      if (need > kScratchBytes)
+        return fail(PARALLAX_ERR_UNSUPPORTED,
+                    "this shape needs " + std::to_string(need) + " bytes of scratch (rho and "
+                    "split states), more than the " + std::to_string(kScratchBytes) +
+                    " bytes of the static scratch array of the allocation-free call");
+      rc = scratch_address(&ws);
+    } else {
+      rc = get_workspace(stream, need, &ws);
+    }
     if (rc != PARALLAX_OK) return rc;
     c.front = front ? ws : nullptr;
     if (states) {
@@ -457,9 +507,10 @@ int setup_decode(const void* q, const float* rho, const void* k_cache, const voi
 }
 
 // Decode (split-K pass) and, for split sequences, the merge.
-int launch_decode_call(const DecodeCall& c, int d, int dtype, int fused, hipStream_t stream) {
+int launch_decode_call(const DecodeCall& c, int d, int dtype, int fused, hipStream_t stream,
+                       bool timed = true) {
   const parallax::DecodeArgs& a = c.a;
-  parallax::LaunchEvents ev = profile_events();
+  parallax::LaunchEvents ev = timed ? profile_events() : parallax::LaunchEvents{};
   hipError_t e =
       (c.p.kernel >= 2)
           ? parallax::launch_decode_mfma(a, d, c.p.kernel == 3 ? 1 : 0, c.p.compact, fused, ev,
@@ -467,7 +518,7 @@ int launch_decode_call(const DecodeCall& c, int d, int dtype, int fused, hipStre
           : parallax::launch_decode_generic(a, d, dtype == PARALLAX_F32 ? 1 : 0, fused, ev, stream);
   profile_record(1, ev, e == hipSuccess);
   if (e == hipSuccess && c.p.splits > 1) {
-    ev = profile_events();
+    ev = timed ? profile_events() : parallax::LaunchEvents{};
     e = parallax::launch_merge(a, d, ev, stream);
     profile_record(2, ev, e == hipSuccess);
   }
@@ -484,6 +535,39 @@ int decode_impl(const void* q, const float* rho, const void* k_cache, const void
                         stream, c);
   if (rc != PARALLAX_OK) return rc;
   return launch_decode_call(c, d, dtype, 0, stream);
+}
+
+// parallax_probe_decode and its allocation-free variant (noalloc: rho and the
+// split states go to the static scratch array; no allocation and no profiling
+// events; shapes whose plan needs more than the array are rejected).
+int probe_decode_impl(const void* W_R, const void* x, const void* q, const void* k_cache,
+                      const void* v_cache, const int* seq_lens, void* out, int B, int Hq, int Hkv,
+                      int d, int d_model, int max_ctx, int dtype, hipStream_t stream,
+                      bool noalloc) {
+  int rc = check_probe(W_R, x, B, Hq, d, d_model, dtype);
+  if (rc != PARALLAX_OK) return rc;
+  rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
+  if (rc != PARALLAX_OK) return rc;
+  const bool fused = fuse_probe(make_plan(B, Hq, Hkv, d, max_ctx, dtype), B, Hq, Hkv, d, d_model,
+                                dtype);
+  DecodeCall c;
+  rc = setup_decode(q, nullptr, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, d, max_ctx, dtype,
+                    fused ? 0 : (size_t)B * Hq * d * sizeof(float), stream, c, noalloc);
+  if (rc != PARALLAX_OK) return rc;
+  if (fused) {
+    c.a.W_R = W_R;
+    c.a.x = x;
+    c.a.d_model = d_model;
+    return launch_decode_call(c, d, dtype, 1, stream, !noalloc);
+  }
+  float* rho = (float*)c.front;
+  const parallax::LaunchEvents ev = noalloc ? parallax::LaunchEvents{} : profile_events();
+  hipError_t e = parallax::launch_probe(W_R, x, rho, B, Hq * d, d_model,
+                                        dtype == PARALLAX_F32 ? 1 : 0, ev, stream);
+  profile_record(0, ev, e == hipSuccess);
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  c.a.rho = rho;
+  return launch_decode_call(c, d, dtype, 0, stream, !noalloc);
 }
 
 }  // namespace
@@ -508,31 +592,19 @@ int parallax_softmax_decode(const void* q, const void* k_cache, const void* v_ca
 int parallax_probe_decode(const void* W_R, const void* x, const void* q, const void* k_cache,
                           const void* v_cache, const int* seq_lens, void* out, int B, int Hq,
                           int Hkv, int d, int d_model, int max_ctx, int dtype, hipStream_t stream) {
-  int rc = check_probe(W_R, x, B, Hq, d, d_model, dtype);
-  if (rc != PARALLAX_OK) return rc;
-  rc = check_decode_shape(B, Hq, Hkv, d, max_ctx, dtype);
-  if (rc != PARALLAX_OK) return rc;
-  const bool fused = fuse_probe(make_plan(B, Hq, Hkv, d, max_ctx, dtype), B, Hq, Hkv, d, d_model,
-                                dtype);
-  DecodeCall c;
-  rc = setup_decode(q, nullptr, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, d, max_ctx, dtype,
-                    fused ? 0 : (size_t)B * Hq * d * sizeof(float), stream, c);
-  if (rc != PARALLAX_OK) return rc;
-  if (fused) {
-    c.a.W_R = W_R;
-    c.a.x = x;
-    c.a.d_model = d_model;
-    return launch_decode_call(c, d, dtype, 1, stream);
-  }
-  float* rho = (float*)c.front;
-  const parallax::LaunchEvents ev = profile_events();
-  hipError_t e = parallax::launch_probe(W_R, x, rho, B, Hq * d, d_model,
-                                        dtype == PARALLAX_F32 ? 1 : 0, ev, stream);
-  profile_record(0, ev, e == hipSuccess);
-  if (e != hipSuccess) return hip_fail(e, "probe launch");
-  c.a.rho = rho;
-  return launch_decode_call(c, d, dtype, 0, stream);
+  return probe_decode_impl(W_R, x, q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, d, d_model,
+                           max_ctx, dtype, stream, false);
 }
+
+int parallax_probe_decode_noalloc(const void* W_R, const void* x, const void* q,
+                                  const void* k_cache, const void* v_cache, const int* seq_lens,
+                                  void* out, int B, int Hq, int Hkv, int d, int d_model,
+                                  int max_ctx, int dtype, hipStream_t stream) {
+  return probe_decode_impl(W_R, x, q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, d, d_model,
+                           max_ctx, dtype, stream, true);
+}
+
+long long parallax_noalloc_scratch_bytes(void) { return (long long)kScratchBytes; }
 
 }  // extern "C"
 

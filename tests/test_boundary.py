@@ -300,3 +300,18 @@ def test_binding_rejects_before_the_library(no_lib):
         pb.prefill(q, None, K, K)
     with pytest.raises(ValueError, match="sink must hold"):
         pb.read_bandwidth(torch.zeros(1 << 20, dtype=torch.uint8), torch.zeros(0, dtype=torch.int32))
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch_array(L):
+    """parallax_probe_decode_noalloc refuses, on the host, a plan whose rho and
+    split states exceed its static scratch array (B = 2048 at 8192 keys: four
+    splits of 16 heads, 136 MB of states), and names the sizes."""
+    args = (16, 16, 16, 16, 16, 16, 16)      # fake, never-dereferenced addresses
+    rc = L.parallax_probe_decode_noalloc(*args, 2048, 16, 8, 128, 2048, 8192, pb.BF16, None)
+    assert rc == pb.ERR_UNSUPPORTED
+    msg = L.parallax_last_error().decode()
+    assert "static scratch array" in msg and str(64 << 20) in msg
+    assert L.parallax_noalloc_scratch_bytes() == 64 << 20
+    # the same shape checks as parallax_probe_decode
+    assert L.parallax_probe_decode_noalloc(*args, 2, 3, 2, 128, 64, 64, pb.BF16, None) == \
+        pb.ERR_INVALID_ARG
