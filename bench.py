@@ -302,6 +302,8 @@ def run_workload(args, wl_id: int, emit: bool = True):
     from parallax_covariance_corrected_amd.workloads import WORKLOADS, make_inputs, algorithmic_bytes
 
     wl = WORKLOADS[wl_id]
+    if args.hq:
+        wl = wl.scaled(Hq=args.hq, name=f"{wl.name}_Hq{args.hq}")
     print(f"# bench: generating {args.sets} input sets for {wl.name}", file=sys.stderr, flush=True)
     sets_host = [make_inputs(wl, seed) for seed in range(args.sets)]
     dev_sets = [upload_set(s) for s in sets_host]
@@ -529,7 +531,7 @@ def run_fusion_sweep(args):
             pb.probe_decode(e["W_R"], e["x"], e["q"], e["K"], e["V"], e["seq_lens"], out=e["out"])
         _, splits, kern = pb.decode_plan(B, Hq, Hkv, d, ctx, code)
         G = Hq // Hkv
-        gh = G if G <= 4 else 4
+        gh = max(g for g in range(1, 9) if G % g == 0)
         item = gh * d * dm * (2 if dt == "bf16" else 4)
         items = B * Hkv * (G // gh) * splits
         with pb.options(fuse=1):
@@ -658,6 +660,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--sets", type=int, default=3)
+    ap.add_argument("--hq", type=int, default=0,
+                    help="query heads of the workload (a multiple of its KV heads): another "
+                         "GQA group size at the same cache")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-configs", dest="configs", action="store_false",
                     help="skip the compact records of the other four workloads")

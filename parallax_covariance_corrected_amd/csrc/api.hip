@@ -211,9 +211,13 @@ int check_decode_shape(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
   return PARALLAX_OK;
 }
 
+// Query heads per work item (each item reads its K/V rows once). Matrix-core
+// kernel: the whole GQA group up to 8 heads, larger groups in blocks of the
+// largest divisor <= 8; generic kernel: blocks of up to 4.
 int head_block(int G, bool mfma) {
-  if (mfma) return G <= 4 ? G : (G % 4 == 0 ? 4 : (G % 3 == 0 ? 3 : (G % 2 == 0 ? 2 : 1)));
-  return (G % 4 == 0) ? 4 : (G % 3 == 0) ? 3 : (G % 2 == 0) ? 2 : 1;
+  for (int gh = mfma ? 8 : 4; gh > 1; --gh)
+    if (G % gh == 0) return gh;
+  return 1;
 }
 
 Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {

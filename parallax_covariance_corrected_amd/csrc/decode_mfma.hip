@@ -9,7 +9,9 @@
 // stream is shared, which is what doubles the arithmetic intensity).
 //
 // Work items. An item is (split of `chunk` keys, sequence, KV head, head block
-// of GH query heads), numbered split-major so that consecutive workgroups —
+// of GH <= 8 query heads: the whole GQA group when it has at most 8 heads, so
+// every K/V row is read once per group), numbered split-major so that
+// consecutive workgroups —
 // which the dispatcher deals round-robin to the 8 XCDs — take different
 // sequences of the same split: the non-empty items of a ragged or sparsely
 // filled cache then spread over every XCD. Two decompositions share the tile
@@ -37,7 +39,8 @@
 //
 // Per tile:
 //  * scores and probes: one bf16 16x16x32 MFMA product K_tile (16 keys x 32
-//    dims) . X^T (32 dims x 16 columns) per 32 dims; the columns of X are q of
+//    dims) . X^T (32 dims x 16 columns) per 32 dims and group of four heads,
+//    all groups multiplying the same K registers; the columns of X are q of
 //    each head (exact: bf16 x bf16 products are exact in fp32) and rho of each
 //    head split as rho_hi + rho_lo in two further columns (summed after the
 //    product, so rho keeps ~16 significant bits). Lane l receives keys
@@ -79,17 +82,42 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
+// Head block of GH <= 8 query heads (one work item), in groups of four: group
+// g holds heads 4g .. 4g + hg(g) - 1 and has a score product of its own (its
+// q, rho_hi and rho_lo columns fill quads 0, 1 and 2 of one 16-column MFMA
+// operand). Its weight rows feed the value-sum MFMAs in one or two "sets" of
+// four rows: a group of one or two heads packs (e_0 .., e p_0 ..) into one set;
+// a group of three or four heads has set A (e_h) and, with the correction,
+// set P (e_h p_h). Without the correction branch (plain softmax attention)
+// only the e rows are accumulated.
 template <int GH, bool CORR>
 struct Layout {
-  // Weight row r of MFMA set `set` -> query head of the block (-1: unused row)
-  // and whether it accumulates A (e v) or P (e p v). Without the correction
-  // branch (plain softmax attention) only the A rows are accumulated.
-  static constexpr int NSET = (GH <= 2 || !CORR) ? 1 : 2;
-  __device__ static constexpr int head(int set, int r) {
-    return GH <= 2 ? (r < GH ? r : (r < 2 * GH ? r - GH : -1)) : (r < GH ? r : -1);
+  static_assert(GH >= 1 && GH <= 8, "head blocks of 1 to 8 query heads");
+  static constexpr int NHG = (GH + 3) / 4;
+  __host__ __device__ static constexpr int hg(int g) { return GH - 4 * g < 4 ? GH - 4 * g : 4; }
+  __host__ __device__ static constexpr bool packed(int g) { return hg(g) <= 2; }
+  __host__ __device__ static constexpr int ns(int g) { return (packed(g) || !CORR) ? 1 : 2; }
+  __host__ __device__ static constexpr int base(int g) {
+    int b = 0;
+    for (int i = 0; i < g; ++i) b += ns(i);
+    return b;
   }
-  __device__ static constexpr bool is_A(int set, int r) {
-    return GH <= 2 ? (r < GH) : (set == 0);
+  static constexpr int NSET = base(NHG);
+  __host__ __device__ static constexpr int group(int set) {
+    int g = 0;
+    while (g + 1 < NHG && base(g + 1) <= set) ++g;
+    return g;
+  }
+  // Weight row r of set `set` -> query head of the block (-1: unused row) and
+  // whether it accumulates A (e v) or P (e p v).
+  __host__ __device__ static constexpr int head(int set, int r) {
+    const int g = group(set), h = hg(g);
+    if (packed(g)) return r < h ? 4 * g + r : (CORR && r < 2 * h ? 4 * g + r - h : -1);
+    return r < h ? 4 * g + r : -1;
+  }
+  __host__ __device__ static constexpr bool is_A(int set, int r) {
+    const int g = group(set);
+    return packed(g) ? r < hg(g) : set == base(g);
   }
 };
 
@@ -114,24 +142,33 @@ struct KV {
 };
 
 // Weighted value sums of key KK of a tile: broadcast block 4*(KK/4) (the lanes
-// holding that key's weight rows) to every block.
-template <int D, int NSET, int KK>
-__device__ __forceinline__ void pv_key(const typename KV<D>::Tile& tl, const float (&w0)[4],
-                                       const float (&w1)[4], f32x4 (&acc)[NSET][KV<D>::TPL]) {
+// holding that key's weight rows) to every block. Set s takes its rows from
+// w0 of its group (packed or A set) or w1 (P set).
+template <int D, int GH, bool CORR, int KK>
+__device__ __forceinline__ void pv_key(const typename KV<D>::Tile& tl,
+                                       const float (&w0)[Layout<GH, CORR>::NHG][4],
+                                       const float (&w1)[Layout<GH, CORR>::NHG][4],
+                                       f32x4 (&acc)[Layout<GH, CORR>::NSET][KV<D>::TPL]) {
+  using L = Layout<GH, CORR>;
   constexpr int ABID = 4 * (KK >> 2), R = KK & 3;
 #pragma unroll
   for (int t = 0; t < KV<D>::TPL; ++t) {
     const float vf = KV<D>::velem(tl.v[KK], t);
-    acc[0][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w0[R], vf, acc[0][t], 4, ABID, 0);
-    if constexpr (NSET > 1)
-      acc[1][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w1[R], vf, acc[1][t], 4, ABID, 0);
+#pragma unroll
+    for (int s = 0; s < L::NSET; ++s) {
+      const int g = L::group(s);
+      const float w = s == L::base(g) ? w0[g][R] : w1[g][R];
+      acc[s][t] = __builtin_amdgcn_mfma_f32_4x4x1f32(w, vf, acc[s][t], 4, ABID, 0);
+    }
   }
 }
-template <int D, int NSET, int... KK>
-__device__ __forceinline__ void pv_tile(const typename KV<D>::Tile& tl, const float (&w0)[4],
-                                        const float (&w1)[4], f32x4 (&acc)[NSET][KV<D>::TPL],
+template <int D, int GH, bool CORR, int... KK>
+__device__ __forceinline__ void pv_tile(const typename KV<D>::Tile& tl,
+                                        const float (&w0)[Layout<GH, CORR>::NHG][4],
+                                        const float (&w1)[Layout<GH, CORR>::NHG][4],
+                                        f32x4 (&acc)[Layout<GH, CORR>::NSET][KV<D>::TPL],
                                         std::integer_sequence<int, KK...>) {
-  (pv_key<D, NSET, KK>(tl, w0, w1, acc), ...);
+  (pv_key<D, GH, CORR, KK>(tl, w0, w1, acc), ...);
 }
 
 // Compacted numbering: item `item` of the call is the item-th non-empty
@@ -248,18 +285,19 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   load(t0, j);
   load(t1, j + STRIDE);
 
-  // Column role of this lane in the score/probe product: quad 0 holds q of
-  // head qi, quad 1 the high and quad 2 the low bf16 half of rho of head qi
-  // (quad 3 and heads >= GH are zero). The value MFMA broadcasts its weight
-  // rows from quad 0 of each 16-lane group, so only quad-0 lanes carry state.
-  const bool is_s = quad == 0 && qi < GH;
+  // Column role of this lane in the score/probe product of head group g:
+  // quad 0 holds q of head 4g + qi, quad 1 the high and quad 2 the low bf16
+  // half of rho of that head (quad 3 and heads past the group are zero). The
+  // value MFMA broadcasts its weight rows from quad 0 of each 16-lane group,
+  // so only quad-0 lanes carry state.
+  constexpr int NHG = L::NHG;
 
-  // B operand at dims 32c + 8*grp + t, staged in LDS and re-read per tile: one
-  // copy per wave for wave items, one per workgroup (written by wave 0) for
-  // workgroup items.
+  // B operands at dims 32c + 8*grp + t, staged in LDS and re-read per tile:
+  // one copy per wave for wave items, one per workgroup (written by wave 0)
+  // for workgroup items.
   constexpr int NBS = WAVE_ITEM ? NW : 1;
   const int bslot = WAVE_ITEM ? wave : 0;
-  __shared__ u32x4 sB[NBS][NC][64];
+  __shared__ u32x4 sB[NBS][NHG][NC][64];
   const float* rsrc = a.rho;
   if constexpr (FUSED) {
     __shared__ __attribute__((aligned(16))) float sR[GH * D];
@@ -269,31 +307,44 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     rsrc = sR;
   }
   if (WAVE_ITEM || wave == 0) {
-    const size_t bh = (size_t)b * a.Hq + h0 + (qi < GH ? qi : 0);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      const size_t off = bh * D + 32 * c + 8 * grp;
-      if (qi < GH && quad == 0) {
-        v = *(const u32x4*)((const uint16_t*)a.q + off);
-      } else if (CORR && qi < GH && (quad == 1 || quad == 2)) {
-        const size_t roff = FUSED ? (size_t)qi * D + 32 * c + 8 * grp : off;
-        const float4 r0 = *(const float4*)(rsrc + roff);
-        const float4 r1 = *(const float4*)(rsrc + roff + 4);
-        const float r[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    for (int g = 0; g < NHG; ++g) {
+      const bool valid = qi < L::hg(g);
+      const int hh = 4 * g + (valid ? qi : 0);   // head within the block
+      const size_t bh = (size_t)b * a.Hq + h0 + hh;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const unsigned hi = pack_bf16x2(r[2 * w], r[2 * w + 1]);
-          v[w] = quad == 1 ? hi : pack_bf16x2(r[2 * w] - bf16_lo(hi), r[2 * w + 1] - bf16_hi(hi));
+      for (int c = 0; c < NC; ++c) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        const size_t off = bh * D + 32 * c + 8 * grp;
+        if (valid && quad == 0) {
+          v = *(const u32x4*)((const uint16_t*)a.q + off);
+        } else if (CORR && valid && (quad == 1 || quad == 2)) {
+          const size_t roff = FUSED ? (size_t)hh * D + 32 * c + 8 * grp : off;
+          const float4 r0 = *(const float4*)(rsrc + roff);
+          const float4 r1 = *(const float4*)(rsrc + roff + 4);
+          const float r[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const unsigned hi = pack_bf16x2(r[2 * w], r[2 * w + 1]);
+            v[w] = quad == 1 ? hi : pack_bf16x2(r[2 * w] - bf16_lo(hi), r[2 * w + 1] - bf16_hi(hi));
+          }
         }
+        sB[bslot][g][c][lane] = v;
       }
-      sB[bslot][c][lane] = v;
     }
   }
   if constexpr (!WAVE_ITEM) __syncthreads();
 
-  float m_run = kNegInf;      // running max (log2 domain), score lanes
-  float lsum = 0.f, ssum = 0.f;
+  // Online state per head group, in the quad-0 lanes of the score columns:
+  // running max (log2 domain), weight sum l and probe-weight sum S (a packed
+  // group keeps S of head h in lane hg + h of lsum).
+  float m_run[NHG], lsum[NHG], ssum[NHG];
+#pragma unroll
+  for (int g = 0; g < NHG; ++g) {
+    m_run[g] = kNegInf;
+    lsum[g] = 0.f;
+    ssum[g] = 0.f;
+  }
   f32x4 acc[NSET][TPL];
 #pragma unroll
   for (int s = 0; s < NSET; ++s)
@@ -301,77 +352,89 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     for (int t = 0; t < TPL; ++t) acc[s][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const typename C::Tile& tl, int jt) {
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sacc[NHG];
+#pragma unroll
+    for (int g = 0; g < NHG; ++g) sacc[g] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tl.k[c]),
-                                                     as_bf16x8(sB[bslot][c][lane]), sacc, 0, 0, 0);
-    float x[4];
-    float lmax = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = is_s ? sacc[r] * a.scale_log2 : kNegInf;
-      lmax = fmaxf(lmax, x[r]);
-    }
-    if (jt + 16 > c1) {   // last tile of the item: mask keys past its end
-      lmax = kNegInf;
+      for (int g = 0; g < NHG; ++g)
+        sacc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(tl.k[c]), as_bf16x8(sB[bslot][g][c][lane]), sacc[g], 0, 0, 0);
+    float w0[NHG][4], w1[NHG][4];
+#pragma unroll
+    for (int g = 0; g < NHG; ++g) {
+      const int hgn = L::hg(g);
+      const bool is_s = quad == 0 && qi < hgn;
+      float x[4];
+      float lmax = kNegInf;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (jt + 4 * grp + r >= c1) x[r] = kNegInf;
+        x[r] = is_s ? sacc[g][r] * a.scale_log2 : kNegInf;
         lmax = fmaxf(lmax, x[r]);
       }
-    }
-    if (__any(is_s && lmax > m_run + kRescaleThreshold)) {
-      float tmax = fmaxf(lmax, __shfl_xor(lmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const bool need = is_s && tmax > m_run + kRescaleThreshold;
-      const float mnew = need ? tmax : m_run;
-      const float alpha = need ? rescale(m_run, mnew) : 1.f;
-      if (is_s) m_run = mnew;
-      float ah[GH];
-#pragma unroll
-      for (int h = 0; h < GH; ++h) ah[h] = readlane_f(alpha, h);
-#pragma unroll
-      for (int s = 0; s < NSET; ++s)
+      if (jt + 16 > c1) {   // last tile of the item: mask keys past its end
+        lmax = kNegInf;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int h = L::head(s, r);
-          if (h < 0) continue;
-#pragma unroll
-          for (int t = 0; t < TPL; ++t) acc[s][t][r] *= ah[h];
+          if (jt + 4 * grp + r >= c1) x[r] = kNegInf;
+          lmax = fmaxf(lmax, x[r]);
         }
-      float a0 = 1.f, a1 = 1.f;
+      }
+      if (__any(is_s && lmax > m_run[g] + kRescaleThreshold)) {
+        float tmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const bool need = is_s && tmax > m_run[g] + kRescaleThreshold;
+        const float mnew = need ? tmax : m_run[g];
+        const float alpha = need ? rescale(m_run[g], mnew) : 1.f;
+        if (is_s) m_run[g] = mnew;
+        float ah[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) ah[h] = h < hgn ? readlane_f(alpha, h) : 1.f;
+#pragma unroll
+        for (int s = L::base(g); s < L::base(g) + L::ns(g); ++s)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int h = L::head(s, r);
+            if (h < 0) continue;
+#pragma unroll
+            for (int t = 0; t < TPL; ++t) acc[s][t][r] *= ah[h - 4 * g];
+          }
+        float a0 = 1.f, a1 = 1.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h0r = L::head(L::base(g), r);
+          if (qi == r && h0r >= 0) a0 = ah[h0r - 4 * g];
+          if (L::ns(g) > 1) {
+            const int h1r = L::head(L::base(g) + 1, r);
+            if (qi == r && h1r >= 0) a1 = ah[h1r - 4 * g];
+          }
+        }
+        lsum[g] *= a0;
+        ssum[g] *= a1;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (qi == r && L::head(0, r) >= 0) a0 = ah[L::head(0, r)];
-        if (NSET > 1 && qi == r && L::head(1, r) >= 0) a1 = ah[L::head(1, r)];
-      }
-      lsum *= a0;
-      ssum *= a1;
-    }
-    float w0[4], w1[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float e = is_s ? fast_exp2(x[r] - m_run) : 0.f;
-      // p = k . (rho_hi + rho_lo): the two halves sit 4 and 8 lanes up.
-      const float p = CORR ? dpp<kDppRowShl4>(sacc[r]) + dpp<kDppRowShl8>(sacc[r]) : 0.f;
-      const float ep = e * p;
-      if constexpr (GH <= 2) {
-        // weight rows (e_0 .. e_{GH-1}, ep_0 .. ep_{GH-1}): lane qi >= GH takes
-        // ep of head qi - GH from its quad.
-        constexpr int kQuadPerm = GH == 2 ? 0x44 : 0x00;
-        const float eps = dpp<kQuadPerm>(ep);
-        w0[r] = qi < GH ? e : (qi < 2 * GH ? eps : 0.f);
-        w1[r] = 0.f;
-        lsum += w0[r];
-      } else {
-        w0[r] = e;
-        w1[r] = ep;
-        lsum += w0[r];
-        if constexpr (CORR) ssum += w1[r];
+        const float e = is_s ? fast_exp2(x[r] - m_run[g]) : 0.f;
+        // p = k . (rho_hi + rho_lo): the two halves sit 4 and 8 lanes up.
+        const float p = CORR ? dpp<kDppRowShl4>(sacc[g][r]) + dpp<kDppRowShl8>(sacc[g][r]) : 0.f;
+        const float ep = e * p;
+        if (L::packed(g)) {
+          // weight rows (e_0 .. e_{hg-1}, ep_0 .. ep_{hg-1}): lane qi >= hg
+          // takes ep of head qi - hg from its quad.
+          const float eps = hgn == 2 ? dpp<0x44>(ep) : dpp<0x00>(ep);
+          w0[g][r] = qi < hgn ? e : (qi < 2 * hgn ? eps : 0.f);
+          w1[g][r] = 0.f;
+          lsum[g] += w0[g][r];
+        } else {
+          w0[g][r] = e;
+          w1[g][r] = ep;
+          lsum[g] += e;
+          if constexpr (CORR) ssum[g] += ep;
+        }
       }
     }
-    pv_tile<D, NSET>(tl, w0, w1, acc, std::make_integer_sequence<int, 16>{});
+    pv_tile<D, GH, CORR>(tl, w0, w1, acc, std::make_integer_sequence<int, 16>{});
   };
 
   // Three-deep ring: compute tile t while tiles t+1, t+2 are loading (deeper
@@ -391,20 +454,24 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   }
 
   // Sum the per-lane weight sums over the four key slots (lane groups of 16).
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if constexpr (NSET > 1) {
-    ssum += __shfl_xor(ssum, 16);
-    ssum += __shfl_xor(ssum, 32);
+#pragma unroll
+  for (int g = 0; g < NHG; ++g) {
+    lsum[g] += __shfl_xor(lsum[g], 16);
+    lsum[g] += __shfl_xor(lsum[g], 32);
+    if (!L::packed(g) && CORR) {
+      ssum[g] += __shfl_xor(ssum[g], 16);
+      ssum[g] += __shfl_xor(ssum[g], 32);
+    }
   }
   // Lane l holds A and P of every head of the block at dims TPL*l + t.
   if constexpr (WAVE_ITEM) {
     float mh[GH], lh[GH], sh[GH];
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
-      mh[h] = readlane_f(m_run, h);
-      lh[h] = readlane_f(lsum, h);
-      sh[h] = (GH <= 2) ? readlane_f(lsum, GH + h) : readlane_f(ssum, h);
+      const int g = h / 4, qh = h % 4;
+      mh[h] = readlane_f(m_run[g], qh);
+      lh[h] = readlane_f(lsum[g], qh);
+      sh[h] = L::packed(g) ? readlane_f(lsum[g], L::hg(g) + qh) : readlane_f(ssum[g], qh);
     }
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
@@ -453,12 +520,19 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
           else sP[wave][h][TPL * lane + t] = acc[s][t][r];
         }
       }
-    if (lane < GH) sM[wave][lane] = m_run;
-    if constexpr (GH <= 2) {
-      if (lane < GH) sL[wave][lane] = lsum;
-      else if (lane < 2 * GH) sS[wave][lane - GH] = lsum;
-    } else {
-      if (lane < GH) { sL[wave][lane] = lsum; sS[wave][lane] = ssum; }
+#pragma unroll
+    for (int g = 0; g < NHG; ++g) {
+      const int hgn = L::hg(g);
+      if (lane < hgn) sM[wave][4 * g + lane] = m_run[g];
+      if (L::packed(g)) {
+        if (lane < hgn) sL[wave][4 * g + lane] = lsum[g];
+        else if (lane < 2 * hgn) sS[wave][4 * g + lane - hgn] = CORR ? lsum[g] : 0.f;
+      } else {
+        if (lane < hgn) {
+          sL[wave][4 * g + lane] = lsum[g];
+          sS[wave][4 * g + lane] = ssum[g];
+        }
+      }
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < GH * D; idx += NW * 64) {
@@ -486,11 +560,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
+// Query heads per work item: the whole GQA group up to 8 heads (one read of
+// each K/V row per group); larger groups in blocks of the largest divisor <= 8.
 int head_block(int G) {
-  if (G <= 4) return G;
-  if (G % 4 == 0) return 4;
-  if (G % 3 == 0) return 3;
-  if (G % 2 == 0) return 2;
+  for (int gh = 8; gh > 1; --gh)
+    if (G % gh == 0) return gh;
   return 1;
 }
 
@@ -502,12 +576,23 @@ hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   const size_t grid = WI ? (items + NW - 1) / NW : items;
   if (grid > 0x7fffffffu || items > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), blk(NW * 64);
+#define PARALLAX_LAUNCH_GH(N)                                                              \
+  case N:                                                                                  \
+    hipExtLaunchKernelGGL((decode_mfma_kernel<D, N, WI, NW, CORR, CP, FU>), g, blk, 0, s,  \
+                          ev.start, ev.stop, 0, a);                                        \
+    break;
   switch (GH) {
-    case 4: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 4, WI, NW, CORR, CP, FU>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 3: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 3, WI, NW, CORR, CP, FU>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 2, WI, NW, CORR, CP, FU>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_mfma_kernel<D, 1, WI, NW, CORR, CP, FU>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    PARALLAX_LAUNCH_GH(8)
+    PARALLAX_LAUNCH_GH(7)
+    PARALLAX_LAUNCH_GH(6)
+    PARALLAX_LAUNCH_GH(5)
+    PARALLAX_LAUNCH_GH(4)
+    PARALLAX_LAUNCH_GH(3)
+    PARALLAX_LAUNCH_GH(2)
+    PARALLAX_LAUNCH_GH(1)
+    default: return hipErrorInvalidValue;
   }
+#undef PARALLAX_LAUNCH_GH
   return hipGetLastError();
 }
 

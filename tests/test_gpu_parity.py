@@ -134,12 +134,14 @@ EDGE_LENS = [0, 1, 15, 16, 17, 127, 128, 129, 300]
 @pytest.mark.parametrize("d,Hq,Hkv,dtype", [(128, 4, 2, "bf16"), (64, 6, 2, "bf16"),
                                             (128, 16, 2, "bf16"), (64, 3, 3, "bf16"),
                                             (128, 32, 2, "bf16"), (64, 20, 4, "bf16"),
-                                            (128, 12, 2, "bf16"),
+                                            (128, 12, 2, "bf16"), (128, 14, 2, "bf16"),
+                                            (64, 8, 1, "bf16"), (128, 24, 3, "bf16"),
                                             (128, 4, 2, "f32"), (64, 2, 1, "f32")])
 def test_edge_lengths(d, Hq, Hkv, dtype):
-    """Lengths 0, 1, tile and chunk boundaries, max; G in {1, 2, 3, 5, 6, 8, 16}
-    (head blocks of 1 to 4 query heads). bf16 runs on the default plan (one
-    split at this cache size) and with 128-key chunks (three splits + merge)."""
+    """Lengths 0, 1, tile and chunk boundaries, max; G in {1, 2, 3, 5, 6, 7, 8,
+    16} (head blocks of 1 to 8 query heads: the whole group up to 8, two blocks
+    of 8 at G = 16). bf16 runs on the default plan (one split at this cache
+    size) and with 128-key chunks (three splits + merge)."""
     wl = WORKLOADS[2].scaled(B=len(EDGE_LENS), Hq=Hq, Hkv=Hkv, d=d, ctx=300, d_model=256,
                              dtype=dtype, wr_std=0.05)
     s = make_inputs(wl, 3, lengths=EDGE_LENS)
@@ -263,7 +265,9 @@ def test_bitwise_repeatable_and_output_guards():
 
 @pytest.mark.parametrize("Hq,Hkv,dtype,kernel,items", [(16, 8, "bf16", 0, 0), (32, 8, "bf16", 0, 0),
                                                       (16, 8, "bf16", 0, 2), (32, 8, "bf16", 2, 1),
-                                                      (12, 4, "bf16", 0, 0), (4, 2, "f32", 0, 0)])
+                                                      (12, 4, "bf16", 0, 0), (64, 8, "bf16", 0, 0),
+                                                      (64, 8, "bf16", 2, 2), (14, 2, "bf16", 0, 0),
+                                                      (4, 2, "f32", 0, 0)])
 def test_softmax_only_variant(Hq, Hkv, dtype, kernel, items):
     """parallax_softmax_decode: plain softmax attention over the same cache (the
     W_R = 0 reduction) against the oracle with rho = 0 and torch SDPA (fp64)."""

@@ -89,10 +89,12 @@ def test_tiny_fp32_workload_runs_fused():
 
 EDGE_LENS = [0, 1, 15, 16, 17, 127, 128, 129, 300]
 
-# (d, Hq, Hkv, dtype, d_model): head blocks of 1 to 4 query heads on both
-# kernels, d_model from one 16-byte piece per row to a ragged number of pieces.
+# (d, Hq, Hkv, dtype, d_model): head blocks of 1 to 8 query heads on the
+# matrix-core kernel (1 to 4 on the generic one), d_model from one 16-byte
+# piece per row to a ragged number of pieces.
 SHAPES = [(128, 4, 2, "bf16", 256), (64, 6, 2, "bf16", 64), (128, 32, 8, "bf16", 128),
           (128, 10, 2, "bf16", 8), (64, 3, 3, "bf16", 2056), (128, 16, 2, "bf16", 136),
+          (64, 14, 2, "bf16", 72), (128, 12, 2, "bf16", 24),
           (128, 4, 2, "f32", 96), (64, 2, 1, "f32", 4), (128, 6, 3, "f32", 260)]
 
 
