@@ -98,7 +98,9 @@ int parallax_probe(const void* W_R, const void* x, float* rho,
  *
  *   q        : [B, Hq, d]               dtype storage (bf16 for both bf16 dtypes)
  *   rho      : [B, Hq, d]               fp32 (from parallax_probe)
- *   k_cache  : [B, Hkv, max_ctx, d]     dtype storage; rows j >= seq_lens[b] are never read
+ *   k_cache  : [B, Hkv, max_ctx, d]     dtype storage; rows j >= seq_lens[b] never
+ *                                       reach the output (the matrix-core kernel may fetch
+ *                                       up to 128 of them per split and discard them)
  *   v_cache  : [B, Hkv, max_ctx, d]     same layout as k_cache
  *   seq_lens : [B] int32, device memory; 0 <= seq_lens[b] <= max_ctx
  *   out      : [B, Hq, d]               fp32 or bf16 per dtype
@@ -284,6 +286,10 @@ int parallax_decode_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
  *                          allows it (generic kernel, or four-wave items
  *                          without the compacted numbering; d_model * element
  *                          size a multiple of 16 bytes)
+ *   PARALLAX_OPT_PREFETCH: matrix-core kernel, first K/V tiles of a work item
+ *                          requested before its sequence length is read:
+ *                          0 = automatic, 1 = never, 2 = wherever the item
+ *                          numbering is not compacted
  */
 typedef enum {
   PARALLAX_OPT_CHUNK = 1,
@@ -291,7 +297,8 @@ typedef enum {
   PARALLAX_OPT_PROFILE = 3,
   PARALLAX_OPT_ITEMS = 4,
   PARALLAX_OPT_ORDER = 5,
-  PARALLAX_OPT_FUSE = 6
+  PARALLAX_OPT_FUSE = 6,
+  PARALLAX_OPT_PREFETCH = 7
 } parallax_option;
 
 int parallax_set_option(int option, int value);

@@ -44,6 +44,7 @@ std::atomic<int> g_opt_profile{0};
 std::atomic<int> g_opt_items{0};
 std::atomic<int> g_opt_order{0};
 std::atomic<int> g_opt_fuse{0};
+std::atomic<int> g_opt_prefetch{0};
 
 // ---------------------------------------------------------------- profiling
 // Start/stop events are handed to hipExtLaunchKernel, which stamps them from
@@ -172,6 +173,7 @@ struct Plan {
   int splits;
   int kernel;   // 1 generic, 2 matrix-core workgroup items, 3 matrix-core wave items
   int compact;  // 1: compacted item numbering (kernel 2 only)
+  int prefetch; // 1: first tiles requested before the sequence length (kernels 2, 3)
 };
 
 // Probe fused into the decode prologue (parallax_probe_decode): every work item
@@ -267,6 +269,15 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
   p.compact = can_compact && B >= 2 && p.splits >= 3 && units * p.splits >= 1024;
   if (g_opt_order == 1) p.compact = 0;
   if (g_opt_order == 2) p.compact = can_compact;
+  // Each item's first two tiles per wave are requested before its sequence's
+  // length arrives (one memory round trip less before the first tile; about
+  // 2 us under load). An empty split then fetches those tiles for nothing, so
+  // the prefetch is left off where many empty splits are possible: the
+  // compacted numbering (which reads all lengths first anyway) and large
+  // batches over several splits.
+  p.prefetch = p.kernel >= 2 && !p.compact && (p.splits <= 2 || B <= 256);
+  if (g_opt_prefetch == 1) p.prefetch = 0;
+  if (g_opt_prefetch == 2) p.prefetch = p.kernel >= 2 && !p.compact;
   return p;
 }
 
@@ -338,6 +349,11 @@ int parallax_set_option(int option, int value) {
       if (value < 0 || value > 2) return fail(PARALLAX_ERR_INVALID_ARG, "fuse must be 0, 1 or 2");
       g_opt_fuse = value;
       return PARALLAX_OK;
+    case PARALLAX_OPT_PREFETCH:
+      if (value < 0 || value > 2)
+        return fail(PARALLAX_ERR_INVALID_ARG, "prefetch must be 0, 1 or 2");
+      g_opt_prefetch = value;
+      return PARALLAX_OK;
 
     default:
       return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
@@ -353,6 +369,7 @@ int parallax_get_option(int option, int* value) {
     case PARALLAX_OPT_ITEMS: *value = g_opt_items; return PARALLAX_OK;
     case PARALLAX_OPT_ORDER: *value = g_opt_order; return PARALLAX_OK;
     case PARALLAX_OPT_FUSE: *value = g_opt_fuse; return PARALLAX_OK;
+    case PARALLAX_OPT_PREFETCH: *value = g_opt_prefetch; return PARALLAX_OK;
     default: return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
   }
 }
@@ -483,6 +500,7 @@ int setup_decode(const void* q, const float* rho, const void* k_cache, const voi
   a.chunk = p.chunk;
   a.splits = p.splits;
   a.out_f32 = (dtype == PARALLAX_BF16) ? 0 : 1;
+  a.prefetch = p.prefetch;
   a.scale_log2 = parallax::kLog2e / sqrtf((float)d);
 
   const size_t front = round_up(front_bytes, 256);

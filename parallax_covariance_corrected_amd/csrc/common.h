@@ -78,19 +78,23 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
 // Split-K partial state of one (sequence, query head, split), fp32:
 //   ml[(b*Hq + h)*splits + s] = {m (log2 domain), l, S, 0}
 //   ap[((b*Hq + h)*splits + s)*2*d + {0: A, d: P} + i]
+// The fields a decode work item needs first (item numbering, its length and
+// K/V addresses) fill the first 64 bytes, one scalar-cache line of the kernel
+// arguments.
 struct DecodeArgs {
-  const void* q;
-  const float* rho;
   const void* k;
   const void* v;
   const int* seq_lens;
-  void* out;
-  float4* ml;
-  float* ap;
   int B, Hq, Hkv, max_ctx;
   int chunk;       // keys per split
   int splits;      // splits per (sequence, KV head)
+  int prefetch = 0;  // matrix-core kernel: first tiles requested before the length arrives
   int out_f32;     // 1: out is fp32, 0: bf16
+  const void* q;
+  const float* rho;
+  void* out;
+  float4* ml;
+  float* ap;
   float scale_log2;  // log2(e) / sqrt(d)
   // Many-query (prefill) form of the generic kernel: when T > 0, sequence b of
   // this call is token b % T of cache sequence b / T and attends to cache rows

@@ -34,8 +34,10 @@
 // Per wave, 16-key tiles stream through a 3-deep register ring: the loads of
 // tiles t+1 and t+2 are in flight while tile t is computed. K/V rows are read
 // with raw buffer loads whose range ends at the last key of the item, so the
-// ragged tail reads zeros without touching memory and nothing past seq_lens is
-// ever read.
+// ragged tail reads zeros without touching memory. With the prefetch flag the
+// wave's first two tiles are requested before the sequence's length is known
+// (ranged to the split's chunk instead), which takes one memory round trip
+// off the start of every item; rows past the length never reach the sums.
 //
 // Per tile:
 //  * scores and probes: one bf16 16x16x32 MFMA product K_tile (16 keys x 32
@@ -255,19 +257,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const int hb = unit_id % hblocks;
   const int kvh = (unit_id / hblocks) % a.Hkv;
   const int b = unit_id / hblocks / a.Hkv;
-  const int n = min(max(a.seq_lens[b], 0), a.max_ctx);
   const int c0 = split * a.chunk;
-  if (split > 0 && c0 >= n) return;   // empty split (split 0 always runs: n = 0 -> out = 0)
-  const int c1 = min(c0 + a.chunk, n);
-  const bool direct = single_chunk(a, n);   // split 0 writes the output itself
+  const int len = a.seq_lens[b];
 
   const int grp = lane >> 4, quad = (lane & 15) >> 2, qi = lane & 3;
   const int h0 = kvh * G + hb * GH;
 
-  // K/V streams of this (sequence, KV head), ranged to [0, c1).
+  // K/V streams of this (sequence, KV head), ranged to the item's keys.
   const size_t seq = ((size_t)b * a.Hkv + kvh) * (size_t)a.max_ctx;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc((const char*)a.k + seq * ROW, (unsigned)c1 * ROW);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const char*)a.v + seq * ROW, (unsigned)c1 * ROW);
+  const char* kbase = (const char*)a.k + seq * ROW;
+  const char* vbase = (const char*)a.v + seq * ROW;
+  __amdgpu_buffer_rsrc_t krs, vrs;
   const unsigned koff = (lane & 15) * ROW + 16 * grp;
   const unsigned voff = lane * (ROW / 64);
   auto load = [&](typename C::Tile& t, int j) {
@@ -279,11 +279,34 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     for (int kk = 0; kk < 16; ++kk) t.v[kk] = C::vload(vrs, base + voff + kk * ROW);
   };
 
-  // Start streaming before the q/rho prologue so the latencies overlap.
+  // The first two tiles of the wave start loading before the q/rho prologue.
+  // With a.prefetch they are issued even before the sequence's length has
+  // arrived, ranged to the split's chunk: rows past the length that they
+  // bring in are zeroed before use (in compute), and an empty split waits for
+  // them and leaves. Otherwise the item's range is known first.
   typename C::Tile t0, t1, t2;
   int j = c0 + (WAVE_ITEM ? 0 : 16 * wave);
-  load(t0, j);
-  load(t1, j + STRIDE);
+  const bool prefetch = !COMPACT && a.prefetch;
+  if (prefetch) {
+    const int cs = min(c0 + a.chunk, a.max_ctx);
+    krs = make_rsrc(kbase, (unsigned)cs * ROW);
+    vrs = make_rsrc(vbase, (unsigned)cs * ROW);
+    load(t0, j);
+    load(t1, j + STRIDE);
+  }
+  const int n = min(max(len, 0), a.max_ctx);
+  if (split > 0 && c0 >= n) {   // empty split (split 0 always runs: n = 0 -> out = 0)
+    if (prefetch) __builtin_amdgcn_s_waitcnt(0);   // no loads in flight at exit
+    return;
+  }
+  const int c1 = min(c0 + a.chunk, n);
+  const bool direct = single_chunk(a, n);   // split 0 writes the output itself
+  krs = make_rsrc(kbase, (unsigned)c1 * ROW);
+  vrs = make_rsrc(vbase, (unsigned)c1 * ROW);
+  if (!prefetch) {
+    load(t0, j);
+    load(t1, j + STRIDE);
+  }
 
   // Column role of this lane in the score/probe product of head group g:
   // quad 0 holds q of head 4g + qi, quad 1 the high and quad 2 the low bf16
@@ -351,7 +374,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < TPL; ++t) acc[s][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const typename C::Tile& tl, int jt) {
+  auto compute = [&](typename C::Tile& tl, int jt) {
+    if (jt + 16 > c1) {   // last tile of the item: zero the rows past its end
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (jt + (lane & 15) >= c1) tl.k[c] = (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk)
+        if (jt + kk >= c1) tl.v[kk] = 0;
+    }
     f32x4 sacc[NHG];
 #pragma unroll
     for (int g = 0; g < NHG; ++g) sacc[g] = (f32x4){0.f, 0.f, 0.f, 0.f};

@@ -150,6 +150,19 @@ def test_edge_lengths(d, Hq, Hkv, dtype):
         _run_full_check(s, tag)
         with pb.options(chunk=128):
             _run_full_check(s, tag + " chunk=128", wr_zero_too=False)
+        # First tiles requested before the lengths arrive (rows past a length
+        # fetched from the NaN padding and zeroed) or after: equal bit for bit.
+        dev = Device(s)
+        rho = dev.probe()
+        outs = []
+        for chunk in (0, 128):
+            for pf in (1, 2):
+                with pb.options(chunk=chunk, prefetch=pf):
+                    outs.append(to64(dev.decode(rho, out_dtype=torch.float32)))
+        torch.cuda.synchronize()
+        for k in (0, 2):
+            assert np.isfinite(outs[k + 1]).all()
+            np.testing.assert_array_equal(outs[k], outs[k + 1])
         return
     say(f"[case] {tag}")
     dev = Device(s)
@@ -216,12 +229,16 @@ def test_compacted_item_order_matches_split_major(B):
     say(f"[case] compacted order B={B} chunk=256")
     dev, dev2 = Device(s), Device(other)
     rho, rho2 = dev.probe(), dev2.probe()
-    with pb.options(chunk=256, order=1, items=1):
+    with pb.options(chunk=256, order=1, items=1, prefetch=1):
         plain = to64(dev.decode(rho, out_dtype=torch.float32))
+    with pb.options(chunk=256, order=1, items=1, prefetch=2):
+        # empty splits among the items, each with its first tiles in flight
+        plain_pf = to64(dev.decode(rho, out_dtype=torch.float32))
     with pb.options(chunk=256, order=2, items=1):
         dev2.decode(rho2, out_dtype=torch.float32)
         comp = to64(dev.decode(rho, out_dtype=torch.float32))
     torch.cuda.synchronize()
+    np.testing.assert_array_equal(plain_pf, plain)
     np.testing.assert_array_equal(comp, plain)
     pairs = sample_pairs(s, 24) + [(0, 0), (1, 3), (5, 7), (B - 1, 7)]
     ref = oracle_out(s, oracle_rho(s), pairs)
