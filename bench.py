@@ -33,29 +33,30 @@ sys.path.insert(0, ROOT)
 METRIC = "Parallax decode tokens/s and HBM GB/s (% of peak) over batch×context sweep"
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak, GB/s
 PROFILES = os.path.join(ROOT, "profiles")
-# The decode kernel's source: its own file and the shared device header.
-DECODE_SRCS = [os.path.join(ROOT, "parallax_covariance_corrected_amd", "csrc", f)
-               for f in ("decode_mfma.hip", "common.h")]
+# Each decode kernel's sources: its own file and the shared device header.
+CSRC = os.path.join(ROOT, "parallax_covariance_corrected_amd", "csrc")
+DECODE_SRCS = {"decode_mfma": ("decode_mfma.hip", "common.h"),
+               "decode_generic": ("decode_generic.hip", "common.h")}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "decode_mfma") -> str:
     h = hashlib.sha256()
-    for f in DECODE_SRCS:
-        h.update(open(f, "rb").read())
+    for f in DECODE_SRCS[kernel]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name: str):
+def measured_traffic(workload_name: str, kernel: str = "decode_mfma"):
     """HBM bytes per decode launch from the committed rocprofv3 PMC summary, or
     None when there is none or the kernel source changed since it was taken."""
-    path = os.path.join(PROFILES, f"decode_mfma_{workload_name}_traffic.md")
+    path = os.path.join(PROFILES, f"{kernel}_{workload_name}_traffic.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"```json\s*(\{.*?\})\s*```", open(path).read(), re.S)
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -303,7 +304,7 @@ def run_workload(args, wl_id: int, emit: bool = True):
 
     wl = WORKLOADS[wl_id]
     if args.hq:
-        wl = wl.scaled(Hq=args.hq, name=f"{wl.name}_Hq{args.hq}")
+        wl = wl.scaled(Hq=args.hq, name=re.sub(r"Hq\d+", f"Hq{args.hq}", wl.name))
     print(f"# bench: generating {args.sets} input sets for {wl.name}", file=sys.stderr, flush=True)
     sets_host = [make_inputs(wl, seed) for seed in range(args.sets)]
     dev_sets = [upload_set(s) for s in sets_host]
@@ -352,7 +353,7 @@ def run_workload(args, wl_id: int, emit: bool = True):
     dec_avg_ms = dec_ms / max(dec_n, 1)
     mrg_avg_ms = mrg_ms / mrg_n if mrg_n else 0.0
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name)
+    traffic = measured_traffic(wl.name, "decode_mfma" if kernel >= 2 else "decode_generic")
     rec = {
         "metric": METRIC,
         "value": round(wl.B / (ms_step * 1e-3), 1),
