@@ -83,6 +83,65 @@ def fill_rho(pb, wl, d):
     pb.probe(d["W_R"], d["x"], wl.Hq, wl.d, out=d["rho"])
 
 
+_SLEEP_CYCLES_PER_US = None
+
+
+def _sleep_cycles_per_us() -> float:
+    """Rate of torch's spin kernel (cycles of its clock per microsecond)."""
+    global _SLEEP_CYCLES_PER_US
+    import torch
+    if _SLEEP_CYCLES_PER_US is None:
+        n = 2_000_000
+        torch.cuda._sleep(n)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(n)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_US = n / max(e0.elapsed_time(e1) * 1e3, 1.0)
+    return _SLEEP_CYCLES_PER_US
+
+
+def per_launch_us(pb, fn, reps: int, kinds):
+    """Average duration in microseconds of each kernel kind in `kinds` over reps
+    calls of fn(i), from per-launch HIP events stamped on the launch stream.
+
+    A per-launch event brackets its kernel only while the stream has work
+    queued ahead of it; when the host enqueues more slowly than the GPU runs,
+    the start stamp can precede the kernel by the host's own launch latency.
+    So the stream is first held by a spin kernel of bounded length (long enough
+    for the host to enqueue all reps calls behind it), and the launches then
+    run back to back as in the timed steps. Returns ({kind: us}, queued), where
+    queued says whether the host had enqueued every call before the spin ended."""
+    import torch
+    rate = _sleep_cycles_per_us()
+    gate = torch.cuda.Event()
+    with pb.options(profile=1):
+        # host cost of one call with its launches stamped
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(min(reps, 20)):
+            fn(i)
+        host_us = (time.perf_counter() - t0) * 1e6 / min(reps, 20)
+        torch.cuda.synchronize()
+        hold_us = min(1.5 * host_us * reps + 2000.0, 500_000.0)
+        pb.profile_reset()
+        torch.cuda._sleep(int(hold_us * rate))
+        gate.record()
+        for i in range(reps):
+            fn(i)
+        queued = not gate.query()
+        torch.cuda.synchronize()
+        out = {}
+        for name, k in kinds:
+            ms, n = pb.profile_read(k)
+            out[name] = ms / n * 1e3 if n else 0.0
+    return out, queued
+
+
 def timed_steps(fn, reps: int, warm: int = 5) -> float:
     """Average microseconds of fn(i) over reps calls, events on the current stream."""
     import torch
@@ -187,18 +246,11 @@ def read_ceiling(pb, reps: int = 30):
     n = 256 << 20
     bufs = [torch.full((n,), i + 1, dtype=torch.uint8, device="cuda") for i in range(3)]
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    for i in range(3):
-        pb.read_bandwidth(bufs[i], sink)
-    torch.cuda.synchronize()
-    pb.profile_reset()
-    with pb.options(profile=1):
-        for i in range(reps):
-            pb.read_bandwidth(bufs[i % 3], sink)
-        torch.cuda.synchronize()
-    ms, cnt = pb.profile_read(pb.KERNEL_READ)
+    us = per_launch_us(pb, lambda i: pb.read_bandwidth(bufs[i % 3], sink), reps,
+                       (("read", pb.KERNEL_READ),))[0]["read"]
     del bufs
     torch.cuda.empty_cache()
-    return n / (ms / cnt * 1e-3) / 1e9
+    return n / (us * 1e-6) / 1e9
 
 
 def step_percentiles(pb, wl, dev_sets, reps: int):
@@ -265,16 +317,9 @@ def run_config(args, wl_id: int, reps: int):
     chunk, splits, kernel = pb.decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.capacity, code)
     fused = pb.probe_decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.d_model, wl.capacity, code)
     step_us = timed_steps(lambda i: step(pb, wl, sets[i % nsets]), reps, warm=max(args.warmup, 3))
-    pb.profile_reset()
-    with pb.options(profile=1):
-        for i in range(reps):
-            step(pb, wl, sets[i % nsets])
-        torch.cuda.synchronize()
-        per = {}
-        for name, k in (("probe", pb.KERNEL_PROBE), ("decode", pb.KERNEL_DECODE),
-                        ("merge", pb.KERNEL_MERGE)):
-            ms, n = pb.profile_read(k)
-            per[name] = ms / n * 1e3 if n else 0.0
+    per, queued = per_launch_us(pb, lambda i: step(pb, wl, sets[i % nsets]), reps,
+                                (("probe", pb.KERNEL_PROBE), ("decode", pb.KERNEL_DECODE),
+                                 ("merge", pb.KERNEL_MERGE)))
     ab = [algorithmic_bytes(wl, t) for t in tokens]
     dec_bytes = sum(a["decode_read"] for a in ab) / len(ab)
     step_bytes = sum(a["total"] for a in ab) / len(ab) + wl.Hq * wl.d * wl.d_model * es
@@ -289,7 +334,7 @@ def run_config(args, wl_id: int, reps: int):
            "frac_decode_call": frac(per["decode"] + per["merge"]),
            "pct_peak_step": round(100 * step_bytes / (step_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
            "mean_tokens_per_set": round(sum(tokens) / len(tokens), 1),
-           "kv_sets_rotated": nsets, "reps": reps,
+           "kv_sets_rotated": nsets, "reps": reps, "launches_queued_ahead": queued,
            "plan": {"chunk": chunk, "splits": splits, "kernel": kernel,
                     "probe": "fused" if fused else "separate"}}
     del sets
@@ -335,14 +380,10 @@ def run_workload(args, wl_id: int, emit: bool = True):
 
     # Same K steps again with per-launch HIP events (stamped by each kernel's
     # dispatch on the launch stream) for the dominant kernel's duration.
-    pb.profile_reset()
-    with pb.options(profile=1):
-        for i in range(args.steps):
-            step(pb, wl, dev_sets[i % len(dev_sets)])
-        torch.cuda.synchronize()
-    dec_ms, dec_n = pb.profile_read(pb.KERNEL_DECODE)
-    mrg_ms, mrg_n = pb.profile_read(pb.KERNEL_MERGE)
-    prb_ms, prb_n = pb.profile_read(pb.KERNEL_PROBE)
+    per, queued = per_launch_us(pb, lambda i: step(pb, wl, dev_sets[i % len(dev_sets)]),
+                                args.steps, (("probe", pb.KERNEL_PROBE),
+                                             ("decode", pb.KERNEL_DECODE),
+                                             ("merge", pb.KERNEL_MERGE)))
 
     ms_step = total_ms / args.steps
     # algorithmic bytes, averaged over the rotated sets
@@ -350,8 +391,8 @@ def run_workload(args, wl_id: int, emit: bool = True):
     ab = [algorithmic_bytes(wl, t) for t in tokens]
     step_bytes = sum(a["total"] for a in ab) / len(ab) + wl.Hq * wl.d * wl.d_model * es
     dec_bytes = sum(a["decode_read"] for a in ab) / len(ab)
-    dec_avg_ms = dec_ms / max(dec_n, 1)
-    mrg_avg_ms = mrg_ms / mrg_n if mrg_n else 0.0
+    dec_avg_ms = per["decode"] * 1e-3
+    mrg_avg_ms = per["merge"] * 1e-3
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
     traffic = measured_traffic(wl.name, "decode_mfma" if kernel >= 2 else "decode_generic")
     rec = {
@@ -385,7 +426,8 @@ def run_workload(args, wl_id: int, emit: bool = True):
                      # the decode call (split-K pass + merge launch) over the same bytes
                      "frac_decode_call": round(dec_bytes / ((dec_avg_ms + mrg_avg_ms) * 1e-3)
                                                / 1e9 / PEAK_HBM_GBS, 4),
-                     "probe_avg_us": round(prb_ms / max(prb_n, 1) * 1e3, 3)},
+                     "probe_avg_us": round(per["probe"], 3),
+                     "launches_queued_ahead": queued},
         "cpu_baseline": None,
     }
     rec["step_time_distribution"] = step_percentiles(pb, wl, dev_sets, args.steps)
@@ -462,17 +504,9 @@ def run_sweep(args):
         t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
         p10, med, p90 = (t[int(f * (reps - 1))] for f in (0.1, 0.5, 0.9))
         # the same calls again with per-launch events: the decode kernel alone
-        pb.profile_reset()
-        with pb.options(profile=1):
-            for i in range(reps):
-                call(i)
-            torch.cuda.synchronize()
-            kms, kn = pb.profile_read(pb.KERNEL_DECODE)
-            for i in range(reps):
-                pb.probe(W_R, x, 16, 128, out=rho)
-            torch.cuda.synchronize()
-            pms, pn = pb.profile_read(pb.KERNEL_PROBE)
-        kus, pus = kms / kn * 1e3, pms / pn * 1e3
+        kus = per_launch_us(pb, call, reps, (("decode", pb.KERNEL_DECODE),))[0]["decode"]
+        pus = per_launch_us(pb, lambda i: pb.probe(W_R, x, 16, 128, out=rho), reps,
+                            (("probe", pb.KERNEL_PROBE),))[0]["probe"]
 
         def step(i):
             K, V = sets[i % nsets]
@@ -573,13 +607,8 @@ def run_prefill(args):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    with pb.options(profile=1):
-        pb.profile_reset()
-        for _ in range(args.steps):
-            pb.prefill(q, rho, K, V, out=out)
-        torch.cuda.synchronize()
-        tot, n = pb.profile_read(pb.KERNEL_PREFILL)
-    kern_us = tot * 1000.0 / max(n, 1)
+    kern_us = per_launch_us(pb, lambda i: pb.prefill(q, rho, K, V, out=out), args.steps,
+                            (("prefill", pb.KERNEL_PREFILL),))[0]["prefill"]
     pairs = Hq * B * T * (T + 1) // 2
     flops = 8 * d * pairs
     achieved = flops / (kern_us * 1e-6) / 1e12
@@ -587,16 +616,8 @@ def run_prefill(args):
     # Matched ratios: the softmax-only forward on the same inputs (same bytes,
     # half the algorithmic flops) and with twice the query heads (same flops).
     def kernel_us(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        with pb.options(profile=1):
-            pb.profile_reset()
-            for _ in range(args.steps):
-                fn()
-            torch.cuda.synchronize()
-            t, c = pb.profile_read(pb.KERNEL_PREFILL)
-        return t * 1000.0 / max(c, 1)
+        return per_launch_us(pb, lambda i: fn(), args.steps,
+                             (("prefill", pb.KERNEL_PREFILL),))[0]["prefill"]
     soft_us = kernel_us(lambda: pb.prefill(q, None, K, V, out=out))
     q2 = torch.randn((B, T, 2 * Hq, d), generator=g, device="cuda").to(torch.bfloat16)
     out2 = torch.empty((B, T, 2 * Hq, d), dtype=torch.bfloat16, device="cuda")
