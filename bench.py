@@ -118,10 +118,12 @@ def per_launch_us(pb, fn, reps: int, kinds):
     rate = _sleep_cycles_per_us()
     gate = torch.cuda.Event()
     with pb.options(profile=1):
-        # host cost of one call with its launches stamped
-        for i in range(3):
+        # one untimed pass creates the library's pooled events, then the host
+        # cost of one call with its launches stamped
+        for i in range(reps):
             fn(i)
         torch.cuda.synchronize()
+        pb.profile_reset()
         t0 = time.perf_counter()
         for i in range(min(reps, 20)):
             fn(i)

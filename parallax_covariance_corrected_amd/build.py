@@ -26,6 +26,8 @@ ARCH = "gfx950"
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-mllvm", "-amdgpu-mfma-vgpr-form",
+             # leading scalar kernel arguments arrive in SGPRs (no argument load)
+             "-mllvm", "-amdgpu-kernarg-preload-count=14",
              "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
 
 

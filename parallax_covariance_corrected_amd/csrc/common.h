@@ -75,12 +75,39 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
   *p = f32_to_bf16_rne(v);
 }
 
+// Kernel arguments in SGPRs. The library is built with kernarg preloading: the
+// leading scalar arguments of a kernel (up to 14 SGPRs) are in SGPRs when its
+// waves start, so a wave does not wait for a load of its argument block before
+// it can address memory. The decode and merge kernels take the fields of
+// DecodeArgs that they need first as such leading arguments (the struct, passed
+// after them, supplies the rest) and write them back into their copy of the
+// struct on entry.
+#define PARALLAX_DECODE_HEAD_PARAMS                                                        \
+  const void *pk_k, const void *pk_v, const int *pk_seq_lens, int pk_B, int pk_Hq,         \
+      int pk_Hkv, int pk_max_ctx, int pk_chunk, int pk_splits, int pk_prefetch
+#define PARALLAX_DECODE_HEAD_ARGS(a)                                                       \
+  (a).k, (a).v, (a).seq_lens, (a).B, (a).Hq, (a).Hkv, (a).max_ctx, (a).chunk, (a).splits,  \
+      (a).prefetch
+#define PARALLAX_DECODE_HEAD_APPLY(a)                                                      \
+  do {                                                                                     \
+    (a).k = pk_k;                                                                          \
+    (a).v = pk_v;                                                                          \
+    (a).seq_lens = pk_seq_lens;                                                            \
+    (a).B = pk_B;                                                                          \
+    (a).Hq = pk_Hq;                                                                        \
+    (a).Hkv = pk_Hkv;                                                                      \
+    (a).max_ctx = pk_max_ctx;                                                              \
+    (a).chunk = pk_chunk;                                                                  \
+    (a).splits = pk_splits;                                                                \
+    (a).prefetch = pk_prefetch;                                                            \
+  } while (0)
+
 // Split-K partial state of one (sequence, query head, split), fp32:
 //   ml[(b*Hq + h)*splits + s] = {m (log2 domain), l, S, 0}
 //   ap[((b*Hq + h)*splits + s)*2*d + {0: A, d: P} + i]
 // The fields a decode work item needs first (item numbering, its length and
-// K/V addresses) fill the first 64 bytes, one scalar-cache line of the kernel
-// arguments.
+// K/V addresses) come first; the kernels also receive them as preloaded
+// leading arguments (PARALLAX_DECODE_HEAD_PARAMS).
 struct DecodeArgs {
   const void* k;
   const void* v;

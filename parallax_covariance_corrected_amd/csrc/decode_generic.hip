@@ -53,7 +53,10 @@ __device__ __forceinline__ void combine(float& m, float& l, float& S, float* A, 
 }
 
 template <bool F32IN, int D, int GB, bool FUSED>
-__global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_generic_kernel(PARALLAX_DECODE_HEAD_PARAMS,
+                                                             DecodeArgs args) {
+  DecodeArgs a = args;
+  PARALLAX_DECODE_HEAD_APPLY(a);
   using E = Elem<F32IN>;
   constexpr int EPL = E::kPerLoad;   // elements per lane
   constexpr int LPK = D / EPL;       // lanes per key
@@ -205,10 +208,10 @@ hipError_t launch_d(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), blk(256);
   switch (GB) {
-    case 4: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 4, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 3: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 3, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 2, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
-    default: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 1, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 4, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, PARALLAX_DECODE_HEAD_ARGS(a), a); break;
+    case 3: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 3, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, PARALLAX_DECODE_HEAD_ARGS(a), a); break;
+    case 2: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 2, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, PARALLAX_DECODE_HEAD_ARGS(a), a); break;
+    default: hipExtLaunchKernelGGL((decode_generic_kernel<F32IN, D, 1, FUSED>), g, blk, 0, s, ev.start, ev.stop, 0, PARALLAX_DECODE_HEAD_ARGS(a), a); break;
   }
   return hipGetLastError();
 }

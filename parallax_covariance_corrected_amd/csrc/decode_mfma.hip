@@ -232,7 +232,10 @@ __device__ __forceinline__ bool compact_item(const DecodeArgs& a, int item, int 
 }
 
 template <int D, int GH, bool WAVE_ITEM, int NW, bool CORR, bool COMPACT, bool FUSED>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(PARALLAX_DECODE_HEAD_PARAMS,
+                                                             DecodeArgs args) {
+  DecodeArgs a = args;
+  PARALLAX_DECODE_HEAD_APPLY(a);
   static_assert(!FUSED || (CORR && !WAVE_ITEM), "the fused probe serves workgroup items");
   using L = Layout<GH, CORR>;
   using C = KV<D>;
@@ -610,7 +613,7 @@ hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
 #define PARALLAX_LAUNCH_GH(N)                                                              \
   case N:                                                                                  \
     hipExtLaunchKernelGGL((decode_mfma_kernel<D, N, WI, NW, CORR, CP, FU>), g, blk, 0, s,  \
-                          ev.start, ev.stop, 0, a);                                        \
+                          ev.start, ev.stop, 0, PARALLAX_DECODE_HEAD_ARGS(a), a);          \
     break;
   switch (GH) {
     PARALLAX_LAUNCH_GH(8)

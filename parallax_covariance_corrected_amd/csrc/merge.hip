@@ -20,7 +20,9 @@ namespace parallax {
 namespace {
 
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void merge_kernel(PARALLAX_DECODE_HEAD_PARAMS, DecodeArgs args) {
+  DecodeArgs a = args;
+  PARALLAX_DECODE_HEAD_APPLY(a);
   constexpr int DPL = D / 64;   // dims per lane
   constexpr int U = 4;          // splits per wave whose loads are in flight together
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -100,8 +102,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
 hipError_t launch_merge(const DecodeArgs& a, int d, LaunchEvents ev, hipStream_t s) {
   const size_t grid = (size_t)a.B * a.Hq;
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  if (d == 64) hipExtLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, ev.start, ev.stop, 0, a);
-  else hipExtLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, ev.start, ev.stop, 0, a);
+  if (d == 64) hipExtLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, ev.start, ev.stop, 0,
+                                        PARALLAX_DECODE_HEAD_ARGS(a), a);
+  else hipExtLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, ev.start, ev.stop, 0,
+                                        PARALLAX_DECODE_HEAD_ARGS(a), a);
   return hipGetLastError();
 }
 
