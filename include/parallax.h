@@ -105,7 +105,8 @@ int parallax_probe(const void* W_R, const void* x, float* rho,
  *   seq_lens : [B] int32, device memory; 0 <= seq_lens[b] <= max_ctx
  *   out      : [B, Hq, d]               fp32 or bf16 per dtype
  *
- * Requires B, Hq, Hkv, max_ctx >= 1, Hq % Hkv == 0, d in {64, 128}. A sequence
+ * Requires B, Hq, Hkv, max_ctx >= 1, Hq % Hkv == 0, d in {64, 128}; Hq above
+ * 65535 is PARALLAX_ERR_UNSUPPORTED (also for the prefill calls). A sequence
  * with seq_lens[b] == 0 gets out = 0 (a convention). seq_lens[b] > max_ctx is
  * clamped to max_ctx and seq_lens[b] < 0 to 0 on the device (memory safety; a
  * caller error).

@@ -210,6 +210,7 @@ int check_decode_shape(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
     return fail(PARALLAX_ERR_UNSUPPORTED, "max_ctx too large for one KV stream (2 GiB)");
   if ((long long)B * Hq > (1LL << 30))
     return fail(PARALLAX_ERR_UNSUPPORTED, "B * Hq too large");
+  if (Hq > 65535) return fail(PARALLAX_ERR_UNSUPPORTED, "Hq too large (at most 65535)");
   return PARALLAX_OK;
 }
 

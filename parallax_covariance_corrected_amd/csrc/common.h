@@ -79,27 +79,31 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
 // leading scalar arguments of a kernel (up to 14 SGPRs) are in SGPRs when its
 // waves start, so a wave does not wait for a load of its argument block before
 // it can address memory. The decode and merge kernels take the fields of
-// DecodeArgs that they need first as such leading arguments (the struct, passed
-// after them, supplies the rest) and write them back into their copy of the
-// struct on entry.
+// DecodeArgs that a work item needs first (K/V, length, q and rho pointers,
+// shape, chunk) as such leading arguments, Hq and Hkv packed into one word
+// (both < 2^16) and the prefetch flag in the top bit of the chunk; the struct,
+// passed after them, supplies the rest. On entry the kernel writes them back
+// into its copy of the struct.
 #define PARALLAX_DECODE_HEAD_PARAMS                                                        \
-  const void *pk_k, const void *pk_v, const int *pk_seq_lens, int pk_B, int pk_Hq,         \
-      int pk_Hkv, int pk_max_ctx, int pk_chunk, int pk_splits, int pk_prefetch
+  const void *pk_k, const void *pk_v, const int *pk_seq_lens, const void *pk_q,            \
+      const float *pk_rho, int pk_B, int pk_max_ctx, unsigned pk_heads, unsigned pk_chunk
 #define PARALLAX_DECODE_HEAD_ARGS(a)                                                       \
-  (a).k, (a).v, (a).seq_lens, (a).B, (a).Hq, (a).Hkv, (a).max_ctx, (a).chunk, (a).splits,  \
-      (a).prefetch
+  (a).k, (a).v, (a).seq_lens, (a).q, (a).rho, (a).B, (a).max_ctx,                          \
+      (unsigned)(a).Hq | ((unsigned)(a).Hkv << 16),                                        \
+      (unsigned)(a).chunk | ((a).prefetch ? 0x80000000u : 0u)
 #define PARALLAX_DECODE_HEAD_APPLY(a)                                                      \
   do {                                                                                     \
     (a).k = pk_k;                                                                          \
     (a).v = pk_v;                                                                          \
     (a).seq_lens = pk_seq_lens;                                                            \
+    (a).q = pk_q;                                                                          \
+    (a).rho = pk_rho;                                                                      \
     (a).B = pk_B;                                                                          \
-    (a).Hq = pk_Hq;                                                                        \
-    (a).Hkv = pk_Hkv;                                                                      \
     (a).max_ctx = pk_max_ctx;                                                              \
-    (a).chunk = pk_chunk;                                                                  \
-    (a).splits = pk_splits;                                                                \
-    (a).prefetch = pk_prefetch;                                                            \
+    (a).Hq = (int)(pk_heads & 0xffffu);                                                    \
+    (a).Hkv = (int)(pk_heads >> 16);                                                       \
+    (a).chunk = (int)(pk_chunk & 0x7fffffffu);                                             \
+    (a).prefetch = (int)(pk_chunk >> 31);                                                  \
   } while (0)
 
 // Split-K partial state of one (sequence, query head, split), fp32:

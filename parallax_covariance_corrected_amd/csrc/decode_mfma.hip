@@ -282,9 +282,42 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(PARALLAX_DECODE_HE
     for (int kk = 0; kk < 16; ++kk) t.v[kk] = C::vload(vrs, base + voff + kk * ROW);
   };
 
-  // The first two tiles of the wave start loading before the q/rho prologue.
-  // With a.prefetch they are issued even before the sequence's length has
-  // arrived, ranged to the split's chunk: rows past the length that they
+  // Column role of this lane in the score/probe product of head group g:
+  // quad 0 holds q of head 4g + qi, quad 1 the high and quad 2 the low bf16
+  // half of rho of that head (quad 3 and heads past the group are zero). The
+  // value MFMA broadcasts its weight rows from quad 0 of each 16-lane group,
+  // so only quad-0 lanes carry state.
+  constexpr int NHG = L::NHG;
+  // The lanes that build the q/rho operand (every wave for wave items, wave 0
+  // for workgroup items) request their q and rho pieces first, all at once:
+  // vector loads complete in order, so issued before the K/V tiles they are
+  // waited for without waiting for the tiles, and issued together (two 16-byte
+  // loads per lane and chunk, from an address chosen per lane, with no branch
+  // whose results would have to be merged before the next load) they cost one
+  // memory round trip. A q lane loads its piece twice; lanes without a piece
+  // load their head's q and ignore it. The fused probe's rho is read from LDS.
+  const bool builder = WAVE_ITEM || wave == 0;
+  u32x4 opc[NHG][NC][2];
+  if (builder) {
+#pragma unroll
+    for (int g = 0; g < NHG; ++g) {
+      const bool valid = qi < L::hg(g);
+      const size_t off = ((size_t)b * a.Hq + h0 + 4 * g + (valid ? qi : 0)) * D + 8 * grp;
+      const bool from_rho = CORR && !FUSED && valid && (quad == 1 || quad == 2);
+      const char* p0 = from_rho ? (const char*)(a.rho + off) : (const char*)((const uint16_t*)a.q + off);
+      const char* p1 = from_rho ? p0 + 16 : p0;
+      const size_t cstep = from_rho ? 32 * sizeof(float) : 32 * sizeof(uint16_t);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        opc[g][c][0] = *(const u32x4*)(p0 + c * cstep);
+        opc[g][c][1] = *(const u32x4*)(p1 + c * cstep);
+      }
+    }
+  }
+
+  // The first two tiles of the wave start loading before the q/rho operand is
+  // built. With a.prefetch they are issued even before the sequence's length
+  // has arrived, ranged to the split's chunk: rows past the length that they
   // bring in are zeroed before use (in compute), and an empty split waits for
   // them and leaves. Otherwise the item's range is known first.
   typename C::Tile t0, t1, t2;
@@ -311,44 +344,40 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(PARALLAX_DECODE_HE
     load(t1, j + STRIDE);
   }
 
-  // Column role of this lane in the score/probe product of head group g:
-  // quad 0 holds q of head 4g + qi, quad 1 the high and quad 2 the low bf16
-  // half of rho of that head (quad 3 and heads past the group are zero). The
-  // value MFMA broadcasts its weight rows from quad 0 of each 16-lane group,
-  // so only quad-0 lanes carry state.
-  constexpr int NHG = L::NHG;
-
   // B operands at dims 32c + 8*grp + t, staged in LDS and re-read per tile:
   // one copy per wave for wave items, one per workgroup (written by wave 0)
   // for workgroup items.
   constexpr int NBS = WAVE_ITEM ? NW : 1;
   const int bslot = WAVE_ITEM ? wave : 0;
   __shared__ u32x4 sB[NBS][NHG][NC][64];
-  const float* rsrc = a.rho;
+  // With the probe fused in, rho of the block's heads is computed into LDS.
+  __shared__ __attribute__((aligned(16))) float sR[FUSED ? GH * D : 1];
   if constexpr (FUSED) {
-    __shared__ __attribute__((aligned(16))) float sR[GH * D];
     probe_rows<false, NW * 64>(a.W_R, (const uint16_t*)a.x + (size_t)b * a.d_model, a.d_model,
                                (size_t)h0 * D, GH * D, sR);
     __syncthreads();
-    rsrc = sR;
   }
-  if (WAVE_ITEM || wave == 0) {
+  if (builder) {
 #pragma unroll
     for (int g = 0; g < NHG; ++g) {
       const bool valid = qi < L::hg(g);
       const int hh = 4 * g + (valid ? qi : 0);   // head within the block
-      const size_t bh = (size_t)b * a.Hq + h0 + hh;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         u32x4 v = {0u, 0u, 0u, 0u};
-        const size_t off = bh * D + 32 * c + 8 * grp;
         if (valid && quad == 0) {
-          v = *(const u32x4*)((const uint16_t*)a.q + off);
+          v = opc[g][c][0];
         } else if (CORR && valid && (quad == 1 || quad == 2)) {
-          const size_t roff = FUSED ? (size_t)hh * D + 32 * c + 8 * grp : off;
-          const float4 r0 = *(const float4*)(rsrc + roff);
-          const float4 r1 = *(const float4*)(rsrc + roff + 4);
-          const float r[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+          u32x4 w0 = opc[g][c][0], w1 = opc[g][c][1];
+          if constexpr (FUSED) {
+            const float* rl = sR + (size_t)hh * D + 32 * c + 8 * grp;
+            w0 = *(const u32x4*)rl;
+            w1 = *(const u32x4*)(rl + 4);
+          }
+          const float r[8] = {__uint_as_float(w0[0]), __uint_as_float(w0[1]),
+                              __uint_as_float(w0[2]), __uint_as_float(w0[3]),
+                              __uint_as_float(w1[0]), __uint_as_float(w1[1]),
+                              __uint_as_float(w1[2]), __uint_as_float(w1[3])};
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const unsigned hi = pack_bf16x2(r[2 * w], r[2 * w + 1]);
