@@ -78,12 +78,12 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
 // Kernel arguments in SGPRs. The library is built with kernarg preloading: the
 // leading scalar arguments of a kernel (up to 14 SGPRs) are in SGPRs when its
 // waves start, so a wave does not wait for a load of its argument block before
-// it can address memory. The decode and merge kernels take the fields of
-// DecodeArgs that a work item needs first (K/V, length, q and rho pointers,
-// shape, chunk) as such leading arguments, Hq and Hkv packed into one word
-// (both < 2^16) and the prefetch flag in the top bit of the chunk; the struct,
-// passed after them, supplies the rest. On entry the kernel writes them back
-// into its copy of the struct.
+// it can address memory. The decode kernels take the fields of DecodeArgs that
+// a work item needs first (K/V, length, q and rho pointers, shape, chunk) as
+// such leading arguments, Hq and Hkv packed into one word (both < 2^16) and
+// the prefetch flag in the top bit of the chunk; the struct, passed after
+// them, supplies the rest. On entry the kernel writes them back into its copy
+// of the struct. (The merge kernel has a head of its own.)
 #define PARALLAX_DECODE_HEAD_PARAMS                                                        \
   const void *pk_k, const void *pk_v, const int *pk_seq_lens, const void *pk_q,            \
       const float *pk_rho, int pk_B, int pk_max_ctx, unsigned pk_heads, unsigned pk_chunk

@@ -330,6 +330,19 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(PARALLAX_DECODE_HE
     load(t0, j);
     load(t1, j + STRIDE);
   }
+  // The other fields the item needs (the score scale, the epilogue's split
+  // count and output type) come from the argument block; an opaque use here
+  // makes the compiler load them now, under the length's wait, rather than
+  // just before their first use (a round trip before the first tile's
+  // scores, and one more at the end of the item).
+  {
+    int sp = a.splits, of = a.out_f32;
+    float sc = a.scale_log2;
+    asm volatile("" : "+s"(sp), "+s"(of), "+s"(sc));
+    a.splits = sp;
+    a.out_f32 = of;
+    a.scale_log2 = sc;
+  }
   const int n = min(max(len, 0), a.max_ctx);
   if (split > 0 && c0 >= n) {   // empty split (split 0 always runs: n = 0 -> out = 0)
     if (prefetch) __builtin_amdgcn_s_waitcnt(0);   // no loads in flight at exit

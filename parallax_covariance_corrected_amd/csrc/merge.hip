@@ -11,61 +11,106 @@
 //
 // One workgroup per (sequence, query head): its 4 waves take interleaved
 // splits, lanes own D/64 dims. Each wave folds its splits with a running max
-// (so the state and partial-sum loads of all its splits are issued together:
-// one memory round trip), then the four wave states are combined through LDS
-// in a fixed order.
+// (the state and partial-sum loads of a batch of its splits are issued
+// together, the first batch before the sequence's length is known: one memory
+// round trip for up to 16 splits), then the four wave states are combined
+// through LDS in a fixed order.
 #include "common.h"
 
 namespace parallax {
 namespace {
 
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(PARALLAX_DECODE_HEAD_PARAMS, DecodeArgs args) {
+// The fields the merge needs first arrive as preloaded leading arguments.
+// SPEC: the first batch of splits is requested before the length (small
+// grids, where the merge's latency is what costs); otherwise a sequence that
+// fits in one chunk leaves at once and no split is read speculatively.
+template <int D, bool SPEC>
+__global__ __launch_bounds__(256) void merge_kernel(const int* pk_seq_lens, float4* pk_ml,
+                                                    float* pk_ap, void* pk_out, int pk_Hq,
+                                                    int pk_max_ctx, int pk_chunk, int pk_splits,
+                                                    int pk_out_f32, DecodeArgs args) {
   DecodeArgs a = args;
-  PARALLAX_DECODE_HEAD_APPLY(a);
+  a.out = pk_out;
+  a.out_f32 = pk_out_f32;
+  a.seq_lens = pk_seq_lens;
+  a.ml = pk_ml;
+  a.ap = pk_ap;
+  a.Hq = pk_Hq;
+  a.max_ctx = pk_max_ctx;
+  a.chunk = pk_chunk;
+  a.splits = pk_splits;
   constexpr int DPL = D / 64;   // dims per lane
   constexpr int U = 4;          // splits per wave whose loads are in flight together
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t bh = blockIdx.x;
   const int b = (int)(bh / a.Hq);
-  const int n = min(max(a.seq_lens[b], 0), a.max_ctx);
-  if (single_chunk(a, n)) return;   // written by the decode kernel
-  const int ns = (n + a.chunk - 1) / a.chunk;
-  const float4* ml = a.ml + bh * a.splits;
-  const float* ap = a.ap + bh * a.splits * 2 * D;
+  // This (sequence, head)'s split states, read through buffer resources over
+  // exactly its own records.
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(a.ml + bh * a.splits, (unsigned)a.splits * 16u);
+  const __amdgpu_buffer_rsrc_t ars =
+      make_rsrc(a.ap + bh * a.splits * 2 * D, (unsigned)a.splits * 2u * D * 4u);
 
   __shared__ float4 sst[4];
   __shared__ float sacc[4][2 * D];
 
+  // A wave takes splits wave, wave + 4, ... in batches of U whose loads are all
+  // in flight at once; the fold has no branch: a split past the sequence's
+  // split count is weighted by zero. With SPEC the first batch is requested
+  // before the length arrives (it may read stale records of splits the
+  // sequence does not have); otherwise batches stop at the sequence's last
+  // split, re-reading it.
+  f32x4 st[U];
+  float av[U][DPL], pv[U][DPL];
+  auto fetch = [&](int s0, int limit) {   // splits past `limit` re-read its last one
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const unsigned s = (unsigned)min(s0 + 4 * u, limit - 1);
+      st[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(mrs, s * 16u, 0, 0));
+      const unsigned off = (s * 2u * D + lane * DPL) * 4u;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        av[u][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ars, off + 4u * k, 0, 0));
+        pv[u][k] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(ars, off + 4u * (D + k), 0, 0));
+      }
+    }
+  };
   // Running state of this wave: max m, and l, S, A, P relative to it.
   float m = kNegInf, l = 0.f, S = 0.f, A[DPL], P[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) { A[k] = 0.f; P[k] = 0.f; }
-  for (int s0 = wave; s0 < ns; s0 += 4 * U) {
-    float4 st[U];
-    float av[U][DPL], pv[U][DPL];
+  auto fold = [&](int s0, int ns) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int s = s0 + 4 * u;
-      st[u] = s < ns ? ml[s] : make_float4(kNegInf, 0.f, 0.f, 0.f);
-      const float* p = ap + (size_t)min(s, ns - 1) * 2 * D + lane * DPL;
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) { av[u][k] = p[k]; pv[u][k] = p[D + k]; }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (s0 + 4 * u >= ns) break;
-      const float mn = fmaxf(m, st[u].x);
-      const float cold = rescale(m, mn), cnew = rescale(st[u].x, mn);
+      const bool ok = s0 + 4 * u < ns;
+      const float mu = ok ? st[u][0] : kNegInf;
+      const float mn = fmaxf(m, mu);
+      const float cold = rescale(m, mn), cnew = rescale(mu, mn);
       m = mn;
-      l = l * cold + cnew * st[u].y;
-      S = S * cold + cnew * st[u].z;
+      l = l * cold + (ok ? cnew * st[u][1] : 0.f);
+      S = S * cold + (ok ? cnew * st[u][2] : 0.f);
 #pragma unroll
       for (int k = 0; k < DPL; ++k) {
-        A[k] = A[k] * cold + cnew * av[u][k];
-        P[k] = P[k] * cold + cnew * pv[u][k];
+        A[k] = A[k] * cold + (ok ? cnew * av[u][k] : 0.f);
+        P[k] = P[k] * cold + (ok ? cnew * pv[u][k] : 0.f);
       }
     }
+  };
+  if constexpr (SPEC) fetch(wave, a.splits);
+  const int n = min(max(a.seq_lens[b], 0), a.max_ctx);
+  // A sequence that fits in one chunk was finished by the decode kernel. With
+  // SPEC the workgroup then folds nothing (ns = 0) and writes nothing: no
+  // early exit, so that the first batch's loads stay ahead of the length.
+  const bool single = single_chunk(a, n);
+  if constexpr (!SPEC) {
+    if (single) return;
+  }
+  const int ns = single ? 0 : (n + a.chunk - 1) / a.chunk;
+  if constexpr (!SPEC) fetch(wave, ns);
+  fold(wave, ns);
+  for (int s0 = wave + 4 * U; s0 < ns; s0 += 4 * U) {
+    fetch(s0, ns);
+    fold(s0, ns);
   }
   if (lane == 0) sst[wave] = make_float4(m, l, S, 0.f);
 #pragma unroll
@@ -92,7 +137,7 @@ __global__ __launch_bounds__(256) void merge_kernel(PARALLAX_DECODE_HEAD_PARAMS,
         At += c[w] * sacc[w][i];
         Pt += c[w] * sacc[w][D + i];
       }
-      store_output(a, bh * D + i, parallax_out(At, Pt, lt, St));
+      if (!single) store_output(a, bh * D + i, parallax_out(At, Pt, lt, St));
     }
   }
 }
@@ -102,10 +147,20 @@ __global__ __launch_bounds__(256) void merge_kernel(PARALLAX_DECODE_HEAD_PARAMS,
 hipError_t launch_merge(const DecodeArgs& a, int d, LaunchEvents ev, hipStream_t s) {
   const size_t grid = (size_t)a.B * a.Hq;
   if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  if (d == 64) hipExtLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)grid), dim3(256), 0, s, ev.start, ev.stop, 0,
-                                        PARALLAX_DECODE_HEAD_ARGS(a), a);
-  else hipExtLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)grid), dim3(256), 0, s, ev.start, ev.stop, 0,
-                                        PARALLAX_DECODE_HEAD_ARGS(a), a);
+  // Speculative first batch for grids of up to one workgroup per compute unit.
+  const bool spec = grid <= 256;
+#define PARALLAX_LAUNCH_MERGE(DD, SP)                                                      \
+  hipExtLaunchKernelGGL((merge_kernel<DD, SP>), dim3((unsigned)grid), dim3(256), 0, s,     \
+                        ev.start, ev.stop, 0, a.seq_lens, a.ml, a.ap, a.out, a.Hq,         \
+                        a.max_ctx, a.chunk, a.splits, a.out_f32, a)
+  if (d == 64) {
+    if (spec) PARALLAX_LAUNCH_MERGE(64, true);
+    else PARALLAX_LAUNCH_MERGE(64, false);
+  } else {
+    if (spec) PARALLAX_LAUNCH_MERGE(128, true);
+    else PARALLAX_LAUNCH_MERGE(128, false);
+  }
+#undef PARALLAX_LAUNCH_MERGE
   return hipGetLastError();
 }
 
