@@ -35,7 +35,7 @@
 // tiles t+1 and t+2 are in flight while tile t is computed. K/V rows are read
 // with raw buffer loads whose range ends at the last key of the item, so the
 // ragged tail reads zeros without touching memory. With the prefetch flag the
-// wave's first two tiles are requested before the sequence's length is known
+// wave's first tile is requested before the sequence's length is known
 // (ranged to the split's chunk instead), which takes one memory round trip
 // off the start of every item; rows past the length never reach the sums.
 //
@@ -46,7 +46,8 @@
 //    each head (exact: bf16 x bf16 products are exact in fp32) and rho of each
 //    head split as rho_hi + rho_lo in two further columns (summed after the
 //    product, so rho keeps ~16 significant bits). Lane l receives keys
-//    4*(l/16) + r, r = 0..3, of column l % 16. X lives in LDS.
+//    4*(l/16) + r, r = 0..3, of column l % 16. Each wave keeps its own copy
+//    of X in LDS.
 //  * online softmax with a lazy rescale: the running max moves only when a
 //    score exceeds it by more than 8 (log2 units), so e <= 2^8 between
 //    rescales; the common path needs no cross-lane reduction.
@@ -288,17 +289,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(PARALLAX_DECODE_HE
   // value MFMA broadcasts its weight rows from quad 0 of each 16-lane group,
   // so only quad-0 lanes carry state.
   constexpr int NHG = L::NHG;
-  // The lanes that build the q/rho operand (every wave for wave items, wave 0
-  // for workgroup items) request their q and rho pieces first, all at once:
-  // vector loads complete in order, so issued before the K/V tiles they are
-  // waited for without waiting for the tiles, and issued together (two 16-byte
-  // loads per lane and chunk, from an address chosen per lane, with no branch
-  // whose results would have to be merged before the next load) they cost one
-  // memory round trip. A q lane loads its piece twice; lanes without a piece
-  // load their head's q and ignore it. The fused probe's rho is read from LDS.
-  const bool builder = WAVE_ITEM || wave == 0;
+  // Every wave builds its own copy of the q/rho operand (so no wave waits at
+  // a workgroup barrier for another's loads) and requests its q and rho
+  // pieces first, all at once: vector loads complete in order, so issued
+  // before the K/V tiles they are waited for without waiting for the tiles,
+  // and issued together (two 16-byte loads per lane and chunk, from an address
+  // chosen per lane, with no branch whose results would have to be merged
+  // before the next load) they cost one memory round trip. A q lane loads its
+  // piece twice; lanes without a piece load their head's q and ignore it. The
+  // fused probe's rho is read from LDS.
   u32x4 opc[NHG][NC][2];
-  if (builder) {
+  {
 #pragma unroll
     for (int g = 0; g < NHG; ++g) {
       const bool valid = qi < L::hg(g);
@@ -315,11 +316,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(PARALLAX_DECODE_HE
     }
   }
 
-  // The first two tiles of the wave start loading before the q/rho operand is
-  // built. With a.prefetch they are issued even before the sequence's length
-  // has arrived, ranged to the split's chunk: rows past the length that they
-  // bring in are zeroed before use (in compute), and an empty split waits for
-  // them and leaves. Otherwise the item's range is known first.
+  // The wave's first tile starts loading before its q/rho operand is built,
+  // and the second once the sequence's length is known. With a.prefetch the
+  // first is issued even before the length has arrived, ranged to the split's
+  // chunk: rows past the length that it brings in are zeroed before use (in
+  // compute), and an empty split waits for it and leaves. Otherwise the
+  // item's range is known first. (Requesting more before the q/rho operand
+  // and the length arrive measured slower: every wave of the launch does so
+  // at once, and those requests queue ahead of the operand's.)
   typename C::Tile t0, t1, t2;
   int j = c0 + (WAVE_ITEM ? 0 : 16 * wave);
   const bool prefetch = !COMPACT && a.prefetch;
@@ -328,7 +332,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(PARALLAX_DECODE_HE
     krs = make_rsrc(kbase, (unsigned)cs * ROW);
     vrs = make_rsrc(vbase, (unsigned)cs * ROW);
     load(t0, j);
-    load(t1, j + STRIDE);
   }
   // The other fields the item needs (the score scale, the epilogue's split
   // count and output type) come from the argument block; an opaque use here
@@ -352,17 +355,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(PARALLAX_DECODE_HE
   const bool direct = single_chunk(a, n);   // split 0 writes the output itself
   krs = make_rsrc(kbase, (unsigned)c1 * ROW);
   vrs = make_rsrc(vbase, (unsigned)c1 * ROW);
-  if (!prefetch) {
-    load(t0, j);
-    load(t1, j + STRIDE);
-  }
+  if (!prefetch) load(t0, j);
+  load(t1, j + STRIDE);
 
-  // B operands at dims 32c + 8*grp + t, staged in LDS and re-read per tile:
-  // one copy per wave for wave items, one per workgroup (written by wave 0)
-  // for workgroup items.
-  constexpr int NBS = WAVE_ITEM ? NW : 1;
-  const int bslot = WAVE_ITEM ? wave : 0;
-  __shared__ u32x4 sB[NBS][NHG][NC][64];
+  // B operands at dims 32c + 8*grp + t, staged in LDS (one copy per wave,
+  // written and read by that wave only) and re-read per tile.
+  __shared__ u32x4 sB[NW][NHG][NC][64];
+  const int bslot = wave;
   // With the probe fused in, rho of the block's heads is computed into LDS.
   __shared__ __attribute__((aligned(16))) float sR[FUSED ? GH * D : 1];
   if constexpr (FUSED) {
@@ -370,7 +369,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(PARALLAX_DECODE_HE
                                (size_t)h0 * D, GH * D, sR);
     __syncthreads();
   }
-  if (builder) {
+  {
 #pragma unroll
     for (int g = 0; g < NHG; ++g) {
       const bool valid = qi < L::hg(g);
@@ -401,7 +400,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(PARALLAX_DECODE_HE
       }
     }
   }
-  if constexpr (!WAVE_ITEM) __syncthreads();
 
   // Online state per head group, in the quad-0 lanes of the score columns:
   // running max (log2 domain), weight sum l and probe-weight sum S (a packed
