@@ -16,8 +16,10 @@
 // sequences of the same split: the non-empty items of a ragged or sparsely
 // filled cache then spread over every XCD. Two decompositions share the tile
 // code:
-//  * workgroup items (long contexts): the 4 waves of a workgroup take
-//    interleaved 16-key tiles of one item and merge their states in LDS;
+//  * workgroup items (long contexts): the 4 waves of a workgroup (8 for head
+//    blocks of 5 to 8 heads, whose value sums cost 2-4x the MFMAs of a small
+//    block) take interleaved 16-key tiles of one item and merge their states
+//    in LDS;
 //  * wave items (short contexts, many sequences): every wave owns one item.
 // With a ragged batch in a large cache many split-major items are empty (the
 // split starts past the sequence's end). In the compacted numbering
@@ -649,12 +651,16 @@ hipError_t launch_dw(const DecodeArgs& a, LaunchEvents ev, hipStream_t s) {
   const size_t items = (size_t)a.B * a.Hkv * (G / GH) * a.splits;
   const size_t grid = WI ? (items + NW - 1) / NW : items;
   if (grid > 0x7fffffffu || items > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  const dim3 g((unsigned)grid), blk(NW * 64);
+  const dim3 g((unsigned)grid);
 #define PARALLAX_LAUNCH_GH(N)                                                              \
-  case N:                                                                                  \
-    hipExtLaunchKernelGGL((decode_mfma_kernel<D, N, WI, NW, CORR, CP, FU>), g, blk, 0, s,  \
+  case N: {                                                                                \
+    /* head blocks of 5-8 heads: 8-wave workgroup items (two waves per SIMD) */            \
+    constexpr int NWX = (!WI && N >= 5) ? 8 : NW;                                          \
+    hipExtLaunchKernelGGL((decode_mfma_kernel<D, N, WI, NWX, CORR, CP, FU>), g,            \
+                          dim3(NWX * 64), 0, s,                                            \
                           ev.start, ev.stop, 0, PARALLAX_DECODE_HEAD_ARGS(a), a);          \
-    break;
+    break;                                                                                 \
+  }
   switch (GH) {
     PARALLAX_LAUNCH_GH(8)
     PARALLAX_LAUNCH_GH(7)
