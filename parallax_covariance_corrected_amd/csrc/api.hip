@@ -231,7 +231,7 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype) {
   if (g_opt_kernel == 1) mfma = false;
   const long long units = (long long)B * Hkv * (G / head_block(G, mfma));
   // Wave items (one wave per item) suit many short sequences; workgroup items
-  // (four waves per item) suit long ones.
+  // (four or eight waves per item) suit long ones.
   bool wave_items = mfma && units >= 1024 && max_ctx <= 1024;
   if (mfma && g_opt_items == 1) wave_items = false;
   if (mfma && g_opt_items == 2) wave_items = true;

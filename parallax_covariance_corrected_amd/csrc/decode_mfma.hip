@@ -684,9 +684,12 @@ hipError_t launch_d(const DecodeArgs& a, int d, int wave_items, int compact, Lau
       return d == 64 ? launch_dw<64, false, 4, true, false, true>(a, ev, s)
                      : launch_dw<128, false, 4, true, false, true>(a, ev, s);
   }
+  // One-wave items go two to a workgroup: a finished wave's slot is refilled
+  // without waiting for three others (4 per workgroup measured 1.5% slower on
+  // the large batch, 1 per workgroup the same as 2).
   if (wave_items)
-    return d == 64 ? launch_dw<64, true, 4, CORR, false>(a, ev, s)
-                   : launch_dw<128, true, 4, CORR, false>(a, ev, s);
+    return d == 64 ? launch_dw<64, true, 2, CORR, false>(a, ev, s)
+                   : launch_dw<128, true, 2, CORR, false>(a, ev, s);
   if (compact)
     return d == 64 ? launch_dw<64, false, 4, CORR, true>(a, ev, s)
                    : launch_dw<128, false, 4, CORR, true>(a, ev, s);
