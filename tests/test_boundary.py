@@ -38,6 +38,8 @@ def _decode(L, *, q=16, rho=16, k=16, v=16, lens=16, out=16, B=2, Hq=4, Hkv=2, d
     (dict(k=24), pb.ERR_INVALID_ARG, "aligned"),
     (dict(lens=18), pb.ERR_INVALID_ARG, "aligned"),
     (dict(max_ctx=1 << 24), pb.ERR_UNSUPPORTED, "max_ctx"),
+    # the kernels receive Hq and Hkv packed into one 32-bit argument
+    (dict(Hq=65536, Hkv=2), pb.ERR_UNSUPPORTED, "65535"),
 ])
 def test_decode_rejects_bad_arguments(L, kw, code, msg):
     assert _decode(L, **kw) == code
@@ -130,6 +132,7 @@ def _prefill(L, *, q=16, rho=16, k=16, v=16, pre=16, out=16, B=2, T=8, Hq=4, Hkv
     (dict(q=24), pb.ERR_INVALID_ARG, "aligned"),
     (dict(pre=18), pb.ERR_INVALID_ARG, "aligned"),
     (dict(B=70000), pb.ERR_UNSUPPORTED, "range"),
+    (dict(Hq=65536, Hkv=1), pb.ERR_UNSUPPORTED, "65535"),
 ])
 def test_prefill_rejects_bad_arguments(L, kw, code, msg):
     assert _prefill(L, **kw) == code
