@@ -287,8 +287,9 @@ int parallax_decode_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
  *                          allows it (generic kernel, or four-wave items
  *                          without the compacted numbering; d_model * element
  *                          size a multiple of 16 bytes)
- *   PARALLAX_OPT_PREFETCH: matrix-core kernel, first K/V tiles of a work item
- *                          requested before its sequence length is read:
+ *   PARALLAX_OPT_PREFETCH: matrix-core kernel, first K/V tile of each wave of a
+ *                          work item requested before the sequence length
+ *                          arrives:
  *                          0 = automatic, 1 = never, 2 = wherever the item
  *                          numbering is not compacted
  */
