@@ -212,21 +212,22 @@ def test_split_and_kernel_invariance(chunk, kernel, items):
     assert rel_l2(o32, ref) <= 1e-5 and max_abs(o32, ref) <= 1e-4
 
 
-@pytest.mark.parametrize("B", [70, 130, 256, 257])
-def test_compacted_item_order_matches_split_major(B):
+@pytest.mark.parametrize("B,Hq", [(70, 8), (130, 8), (256, 8), (257, 8), (130, 16)])
+def test_compacted_item_order_matches_split_major(B, Hq):
     """Numbering only the non-empty work items (a ragged batch in a cache of
     many chunks; sequences in two to four groups of 64) computes the same
     items as the split-major numbering of every item: equal bit for bit, and
     right against the oracle when the workspace still holds another input's
     partial states (an item left out would leave one of those behind). At
     B = 257 the compacted numbering does not apply and the option falls back
-    to split-major."""
-    wl = WORKLOADS[5].scaled(B=B, Hq=8, Hkv=2, ctx=2000, d_model=256)
+    to split-major. Hq = 16 over 2 KV heads runs head blocks of 8 (eight-wave
+    workgroup items)."""
+    wl = WORKLOADS[5].scaled(B=B, Hq=Hq, Hkv=2, ctx=2000, d_model=256)
     r = np.random.default_rng(B)
     lens = [0, 1, 255, 256, 257, 2000] + [int(x) for x in r.integers(0, 2001, B - 6)]
     s = make_inputs(wl, 21, lengths=lens)
     other = make_inputs(wl, 22, lengths=[2000] * B)
-    say(f"[case] compacted order B={B} chunk=256")
+    say(f"[case] compacted order B={B} Hq={Hq} chunk=256")
     dev, dev2 = Device(s), Device(other)
     rho, rho2 = dev.probe(), dev2.probe()
     with pb.options(chunk=256, order=1, items=1, prefetch=1):
