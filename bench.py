@@ -457,8 +457,8 @@ def run_sweep(args):
     """Batch x context sweep at Hq=16, Hkv=8, d=128, d_model=2048, bf16. Per point,
     on rotated K/V sets (so that every call reads cold data): the decode call
     (split-K pass + merge) timed over 100 calls after 20 warm-up calls, each call
-    bracketed by its own events (median, p10, p90), and the decode kernel's own
-    duration (per-launch events); the probe alone and the whole step through
+    bracketed by its own events (median, p10, p90), the same calls back to back
+    (mean per call), and the decode kernel's own duration (per-launch events); the probe alone and the whole step through
     parallax_probe_decode (mean over 100 steps); the share of the correction in
     the output, ||C rho|| / ||out||. One JSON line per point. GB/s counts K/V,
     q, rho, out and seq_lens; `pct_peak` is over the decode call's median,
@@ -505,7 +505,9 @@ def run_sweep(args):
         torch.cuda.synchronize()
         t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
         p10, med, p90 = (t[int(f * (reps - 1))] for f in (0.1, 0.5, 0.9))
-        # the same calls again with per-launch events: the decode kernel alone
+        # the same calls back to back (mean per call), then with per-launch
+        # events: the decode kernel alone
+        b2b = timed_steps(call, reps, warm=5)
         kus = per_launch_us(pb, call, reps, (("decode", pb.KERNEL_DECODE),))[0]["decode"]
         pus = per_launch_us(pb, lambda i: pb.probe(W_R, x, 16, 128, out=rho), reps,
                             (("probe", pb.KERNEL_PROBE),))[0]["probe"]
@@ -530,6 +532,7 @@ def run_sweep(args):
                           "tokens_per_s": round(B / (med * 1e-6), 1),
                           "gbps": round(byts / (med * 1e-6) / 1e9, 1),
                           "pct_peak": pct(med),
+                          "call_us_back_to_back": round(b2b, 2), "call_pct_peak_back_to_back": pct(b2b),
                           "kernel_us": round(kus, 2), "kernel_pct_peak": pct(kus),
                           "probe_us": round(pus, 2), "probe_decode_step_us": round(step_us, 2),
                           "correction_to_output": round(corr, 4)}),
