@@ -183,15 +183,18 @@ struct Plan {
 // probe launch (a few microseconds whatever its size) only where the reads per
 // item and in total stay small. Limits from timing whole steps both ways over
 // batch 1-64 x d_model 64-2048 x context 128-4096 (Hq 16, Hkv 8, d 128, bf16;
-// and fp32 shapes), three runs: on the matrix-core kernel the fused step took
-// 0.74-0.98x the separate one at 32 KiB of W_R per item (up to 16 MiB in
-// all), 0.88-1.17x at 64 KiB, and more beyond (up to 2.6x at 1 MiB per item);
-// on the generic kernel, whose decode is slower and hides more of the
-// prologue, 0.74-0.94x up to 128 KiB per item.
+// and fp32 shapes): on the matrix-core kernel the fused step took 0.73-1.01x
+// the separate one at 32 KiB of W_R per item (up to 16 MiB in all),
+// 0.78-0.86x at 64 KiB per item up to 8 MiB in all (0.84-1.20x beyond),
+// 0.86-0.91x at 128 KiB per item up to 4 MiB in all (0.93-1.23x beyond), and
+// more at larger rows (up to 2.3x at 1 MiB per item); on the generic kernel,
+// whose decode is slower and hides more of the prologue, 0.75-0.94x up to
+// 128 KiB per item.
 struct FuseLimit {
   long long item_bytes, total_bytes;
 };
-constexpr FuseLimit kFuseMfma[] = {{32LL << 10, 16LL << 20}};
+constexpr FuseLimit kFuseMfma[] = {{32LL << 10, 16LL << 20}, {64LL << 10, 8LL << 20},
+                                   {128LL << 10, 4LL << 20}};
 constexpr FuseLimit kFuseGeneric[] = {{128LL << 10, 8LL << 20}};
 
 int esize(int dtype) { return dtype == PARALLAX_F32 ? 4 : 2; }

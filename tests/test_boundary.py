@@ -89,13 +89,17 @@ def test_probe_decode_plan():
     for shape in [(16, 16, 8, 128, 2048, 4096), (1, 16, 8, 128, 2048, 32768),
                   (2048, 16, 8, 128, 2048, 128), (64, 32, 8, 128, 2560, 32768)]:
         assert not pb.probe_decode_plan(*shape, pb.BF16)
-    # small d_model and few items: fused (32 KiB per item, up to 16 MiB in
-    # all); more: separate
+    # small d_model and few items: fused (32 KiB per item up to 16 MiB in all,
+    # 64 KiB up to 8 MiB, 128 KiB up to 4 MiB); more: separate
     assert pb.probe_decode_plan(4, 16, 8, 128, 64, 1024, pb.BF16)          # 32 KiB x 256
     assert pb.probe_decode_plan(64, 16, 8, 128, 64, 128, pb.BF16)          # 32 KiB x 512
-    assert not pb.probe_decode_plan(1, 16, 8, 128, 128, 128, pb.BF16)      # 64 KiB x 8
+    assert pb.probe_decode_plan(1, 16, 8, 128, 128, 128, pb.BF16)          # 64 KiB x 8
+    assert pb.probe_decode_plan(16, 16, 8, 128, 128, 128, pb.BF16)         # 64 KiB x 128
+    assert not pb.probe_decode_plan(4, 16, 8, 128, 128, 4096, pb.BF16)     # 64 KiB x 256
+    assert pb.probe_decode_plan(4, 16, 8, 128, 256, 128, pb.BF16)          # 128 KiB x 32
+    assert not pb.probe_decode_plan(1, 16, 8, 128, 256, 1024, pb.BF16)     # 128 KiB x 64
     assert not pb.probe_decode_plan(64, 16, 8, 128, 64, 4096, pb.BF16)     # 32 KiB x 1024
-    assert not pb.probe_decode_plan(1, 16, 8, 128, 256, 128, pb.BF16)      # 128 KiB
+    assert not pb.probe_decode_plan(1, 16, 8, 128, 512, 128, pb.BF16)      # 256 KiB
     assert not pb.probe_decode_plan(256, 16, 8, 128, 64, 1024, pb.BF16)
     # the generic kernel (fp32): up to 128 KiB per item, 8 MiB in all
     assert pb.probe_decode_plan(4, 2, 2, 64, 512, 1024, pb.F32)            # 128 KiB x 64
