@@ -24,9 +24,9 @@
 // With a ragged batch in a large cache many split-major items are empty (the
 // split starts past the sequence's end). In the compacted numbering
 // (workgroup items, up to 256 sequences) workgroup i takes the i-th non-empty
-// item of the split-major order instead, so the workgroups that find nothing
-// form one run at the end of the grid rather than being interleaved with
-// working ones.
+// item instead, longest first, so the workgroups that find nothing form one
+// run at the end of the grid rather than being interleaved with working ones
+// and the shortest items fill the end of the launch.
 // With the probe fused in (workgroup items only), the workgroup computes rho
 // of its head block from W_R and x into LDS while its first K/V tiles load.
 // A sequence that fits in one chunk gets its output written directly;
@@ -176,13 +176,18 @@ __device__ __forceinline__ void pv_tile(const typename KV<D>::Tile& tl,
   (pv_key<D, GH, CORR, KK>(tl, w0, w1, acc), ...);
 }
 
-// Compacted numbering: item `item` of the call is the item-th non-empty
-// (split, unit) pair in split-major order, where a unit is one of the `ups`
-// (KV head, head block) pairs of a sequence and split s >= 1 of sequence b is
-// non-empty when it starts before the sequence's end (split 0 always runs).
-// Every wave of the workgroup computes the same answer from the B lengths
+// Compacted numbering: the call's items are the non-empty (split, unit)
+// pairs, where a unit is one of the `ups` (KV head, head block) pairs of a
+// sequence and split s >= 1 of sequence b is non-empty when it starts before
+// the sequence's end (split 0 always runs). They are numbered longest first,
+// so that the short ones fill the end of the launch: every full chunk in
+// split-major order, then the sequences' shorter last chunks in
+// kTailClasses classes of remaining length, longest class first (a
+// zero-length sequence's one item falls in the last class). Every wave of the
+// workgroup computes the same answer from the B lengths
 // (B <= 64 * kCompactGroups); returns false when the item does not exist.
 constexpr int kCompactGroups = 4;
+constexpr int kTailClasses = 8;
 __device__ __forceinline__ bool compact_item(const DecodeArgs& a, int item, int ups, int& split,
                                              int& unit_id) {
   const int lane = threadIdx.x & 63;
@@ -200,13 +205,20 @@ __device__ __forceinline__ bool compact_item(const DecodeArgs& a, int item, int 
   for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o);
   if (item >= mine * ups) return false;
   int base = 0;
-  for (int s = 0; s < a.splits; ++s) {
-    const int lo = s * a.chunk;
+  // Rounds 0 .. splits-1 take the full chunks of split s; the following
+  // kTailClasses rounds take the partial last chunks, class by class.
+  for (int s = 0; s < a.splits + kTailClasses; ++s) {
+    const bool tail = s >= a.splits;
+    const int cls = kTailClasses - 1 - (s - a.splits);
     unsigned long long m[kCompactGroups];
     int cnt = 0;
 #pragma unroll
     for (int g = 0; g < kCompactGroups; ++g) {
-      m[g] = g < groups ? __ballot(s == 0 ? n[g] >= 0 : n[g] > lo) : 0ull;
+      const int rem = n[g] % a.chunk;   // keys in the last chunk when partial
+      const bool partial = n[g] == 0 || rem > 0;
+      const bool have = tail ? n[g] >= 0 && partial && (kTailClasses * rem) / a.chunk == cls
+                             : n[g] >= (s + 1) * a.chunk;
+      m[g] = g < groups ? __ballot(have) : 0ull;
       cnt += __popcll(m[g]);
     }
     const int span = cnt * ups;
@@ -221,8 +233,11 @@ __device__ __forceinline__ bool compact_item(const DecodeArgs& a, int item, int 
           const unsigned below = __builtin_amdgcn_mbcnt_hi(
               (unsigned)(m[g] >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m[g], 0u));
           const unsigned long long hit = __ballot(((m[g] >> lane) & 1ull) && (int)below == r);
-          const int b = 64 * g + __builtin_ctzll(hit);
-          split = __builtin_amdgcn_readfirstlane(s);
+          const int l = __builtin_ctzll(hit);
+          const int b = 64 * g + l;
+          // a partial chunk is its sequence's last split
+          split = tail ? __builtin_amdgcn_readlane(n[g], l) / a.chunk
+                       : __builtin_amdgcn_readfirstlane(s);
           unit_id = __builtin_amdgcn_readfirstlane(b * ups + within);
           return true;
         }
