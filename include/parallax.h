@@ -292,6 +292,10 @@ int parallax_decode_plan(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
  *                          arrives:
  *                          0 = automatic, 1 = never, 2 = wherever the item
  *                          numbering is not compacted
+ *   PARALLAX_OPT_PROBE   : bf16 probe kernel (parallax_probe and the separate
+ *                          probe of parallax_probe_decode): 0 = automatic,
+ *                          1 = the small-batch matrix-core kernel (row blocks
+ *                          of at most 64 rows), 2 = the LDS-tiled GEMM
  */
 typedef enum {
   PARALLAX_OPT_CHUNK = 1,
@@ -300,7 +304,8 @@ typedef enum {
   PARALLAX_OPT_ITEMS = 4,
   PARALLAX_OPT_ORDER = 5,
   PARALLAX_OPT_FUSE = 6,
-  PARALLAX_OPT_PREFETCH = 7
+  PARALLAX_OPT_PREFETCH = 7,
+  PARALLAX_OPT_PROBE = 8
 } parallax_option;
 
 int parallax_set_option(int option, int value);

@@ -45,6 +45,7 @@ std::atomic<int> g_opt_items{0};
 std::atomic<int> g_opt_order{0};
 std::atomic<int> g_opt_fuse{0};
 std::atomic<int> g_opt_prefetch{0};
+std::atomic<int> g_opt_probe{0};
 
 // ---------------------------------------------------------------- profiling
 // Start/stop events are handed to hipExtLaunchKernel, which stamps them from
@@ -358,6 +359,10 @@ int parallax_set_option(int option, int value) {
         return fail(PARALLAX_ERR_INVALID_ARG, "prefetch must be 0, 1 or 2");
       g_opt_prefetch = value;
       return PARALLAX_OK;
+    case PARALLAX_OPT_PROBE:
+      if (value < 0 || value > 2) return fail(PARALLAX_ERR_INVALID_ARG, "probe must be 0, 1 or 2");
+      g_opt_probe = value;
+      return PARALLAX_OK;
 
     default:
       return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
@@ -374,6 +379,7 @@ int parallax_get_option(int option, int* value) {
     case PARALLAX_OPT_ORDER: *value = g_opt_order; return PARALLAX_OK;
     case PARALLAX_OPT_FUSE: *value = g_opt_fuse; return PARALLAX_OK;
     case PARALLAX_OPT_PREFETCH: *value = g_opt_prefetch; return PARALLAX_OK;
+    case PARALLAX_OPT_PROBE: *value = g_opt_probe; return PARALLAX_OK;
     default: return fail(PARALLAX_ERR_INVALID_ARG, "unknown option " + std::to_string(option));
   }
 }
@@ -423,7 +429,7 @@ int parallax_probe(const void* W_R, const void* x, float* rho, int B, int Hq, in
   if (!aligned(rho, 16)) return fail(PARALLAX_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   const parallax::LaunchEvents ev = profile_events();
   hipError_t e = parallax::launch_probe(W_R, x, rho, B, Hq * d, d_model,
-                                        dtype == PARALLAX_F32 ? 1 : 0, ev, stream);
+                                        dtype == PARALLAX_F32 ? 1 : 0, g_opt_probe, ev, stream);
   profile_record(0, ev, e == hipSuccess);
   if (e != hipSuccess) return hip_fail(e, "probe launch");
   return PARALLAX_OK;
@@ -589,7 +595,7 @@ int probe_decode_impl(const void* W_R, const void* x, const void* q, const void*
   float* rho = (float*)c.front;
   const parallax::LaunchEvents ev = noalloc ? parallax::LaunchEvents{} : profile_events();
   hipError_t e = parallax::launch_probe(W_R, x, rho, B, Hq * d, d_model,
-                                        dtype == PARALLAX_F32 ? 1 : 0, ev, stream);
+                                        dtype == PARALLAX_F32 ? 1 : 0, g_opt_probe, ev, stream);
   profile_record(0, ev, e == hipSuccess);
   if (e != hipSuccess) return hip_fail(e, "probe launch");
   c.a.rho = rho;

@@ -239,7 +239,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int d, int wave_items, int co
 hipError_t launch_merge(const DecodeArgs& a, int d, LaunchEvents ev, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int d, LaunchEvents ev, hipStream_t s);
 bool decode_mfma_supported(int d, int G);
+// path (bf16): 0 = automatic, 1 = the small-batch kernel (row blocks of at
+// most 64), 2 = the LDS-tiled GEMM.
 hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, int K,
-                        int f32_inputs, LaunchEvents ev, hipStream_t s);
+                        int f32_inputs, int path, LaunchEvents ev, hipStream_t s);
 
 }  // namespace parallax

@@ -12,8 +12,9 @@
 // 16 columns tile and loads its operands straight from memory into MFMA
 // registers; its waves split K NW ways, each issuing the loads of U k-steps
 // before their MFMAs, and reduce through LDS in a fixed order. Rows past B
-// read zeros (buffer range). Larger batches (B > 64): an LDS-tiled GEMM with
-// 128 x 128 tiles (below), where operand reuse across waves pays for staging.
+// read zeros (buffer range); B up to 128 runs as row blocks of this kernel.
+// Larger batches (B > 128): an LDS-tiled GEMM with 128 x 128 tiles (below),
+// where operand reuse across waves pays for staging.
 // fp32 kernel: one wave per output, a plain dot product.
 #include <type_traits>
 
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256) void probe_f32_kernel(const float* __restrict_
 }  // namespace
 
 hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, int K,
-                        int f32_inputs, LaunchEvents ev, hipStream_t s) {
+                        int f32_inputs, int path, LaunchEvents ev, hipStream_t s) {
   if (f32_inputs) {
     const size_t total = (size_t)B * N;
     const size_t grid = (total + 3) / 4;
@@ -274,15 +275,24 @@ hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, 
   }
   const uint16_t* Wb = (const uint16_t*)W;
   const uint16_t* xb = (const uint16_t*)x;
-  if (B > 64) {
+  // The tiled GEMM has few workgroups below a few hundred rows (one per 128 x
+  // 128 tile), each waiting out a memory round trip per K step: 19-21 us at
+  // B = 64-256 for a cold 2048 x 2048 W_R, against 7.4 / 12.8 / 23.5 us for
+  // the small-batch kernel at B = 64 / 128 / 256, whose cost grows with the
+  // row blocks (4096 x 2560: 15.6 / 27.3 / 51 against 28-32 us).
+  const bool gemm = path == 2 || (path == 0 && B > 128);
+  if (gemm) {
     dim3 grid((N + kGN - 1) / kGN, (B + kGM - 1) / kGM);
+    if (grid.y > 65535u) return hipErrorInvalidConfiguration;
     hipExtLaunchKernelGGL(probe_gemm_kernel, grid, dim3(kGThreads), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
   } else {
     // Shapes picked by a sweep over cold W_R (tiles of 8 / 16 columns, 4-16
     // waves, 2-8 k-steps in flight): aim for at least 256 workgroups, since a
-    // workgroup's read of its W_R rows is latency-bound.
-    const int mt = (B + 15) / 16;
-    dim3 grid((N + 15) / 16, 1);
+    // workgroup's read of its W_R rows is latency-bound. Batches above 64 rows
+    // take row blocks of 64 (32 with few column tiles) on grid.y.
+    const int mt = min((B + 15) / 16, 4);
+    dim3 grid((N + 15) / 16, (unsigned)((B + 16 * mt - 1) / (16 * mt)));
+    if ((B + 31) / 32 > 65535) return hipErrorInvalidConfiguration;
     if (mt == 1) {
       grid.x = (N + 7) / 8;
       hipExtLaunchKernelGGL((probe_mfma_kernel<1, 1, 16, 4, 8>), grid, dim3(1024), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);

@@ -165,6 +165,11 @@ def test_options_and_profile_on_host(L):
     assert L.parallax_set_option(pb.OPT_ITEMS, 3) == pb.ERR_INVALID_ARG
     assert L.parallax_set_option(99, 0) == pb.ERR_INVALID_ARG
     assert L.parallax_set_option(pb.OPT_ORDER, 3) == pb.ERR_INVALID_ARG
+    assert L.parallax_set_option(pb.OPT_PROBE, 3) == pb.ERR_INVALID_ARG
+    assert L.parallax_set_option(pb.OPT_PROBE, -1) == pb.ERR_INVALID_ARG
+    with pb.options(probe=2):
+        assert pb.get_option(pb.OPT_PROBE) == 2
+    assert pb.get_option(pb.OPT_PROBE) == 0
     with pb.options(chunk=512, kernel=1):
         assert pb.get_option(pb.OPT_CHUNK) == 512 and pb.get_option(pb.OPT_KERNEL) == 1
         assert pb.decode_plan(16, 16, 8, 128, 4096) == (512, 8, 1)

@@ -338,13 +338,20 @@ def test_workspace_grows_across_shapes_and_streams():
     (1, 2048, "bf16", 16, 128), (17, 2560, "bf16", 16, 128), (64, 2048, "bf16", 16, 128),
     (65, 512, "bf16", 16, 128), (130, 72, "bf16", 16, 128), (3, 100, "f32", 16, 128),
     (2048, 2048, "bf16", 16, 128), (300, 520, "bf16", 3, 64), (129, 4096, "bf16", 5, 128),
-    (40, 2048, "bf16", 16, 128), (48, 1024, "bf16", 32, 128), (33, 264, "bf16", 5, 64)])
+    (40, 2048, "bf16", 16, 128), (48, 1024, "bf16", 32, 128), (33, 264, "bf16", 5, 64),
+    (128, 2560, "bf16", 32, 128), (97, 264, "bf16", 6, 64)])
 def test_probe_shapes(B, d_model, dtype, Hq, d):
+    """Automatic kernel choice, then (bf16) each of the two probe kernels forced:
+    the small-batch kernel in row blocks and the tiled GEMM, at every batch."""
     wl = WORKLOADS[2].scaled(B=B, d_model=d_model, ctx=16, dtype=dtype, Hq=Hq, Hkv=1, d=d)
     s = make_inputs(wl, 7)
-    say(f"[case] probe B={B} d_model={d_model} Hq={Hq} d={d} {dtype}")
-    rho = pb.probe(s.W_R.cuda(), s.x.cuda(), wl.Hq, wl.d)
-    torch.cuda.synchronize()
-    e = rel_l2(to64(rho), oracle_rho(s))
-    say(f"probe B={B} d_model={d_model}: rel {e:.3e}")
-    assert e <= RHO_REL_L2
+    W, x = s.W_R.cuda(), s.x.cuda()
+    want = oracle_rho(s)
+    for path in ((0, 1, 2) if dtype == "bf16" else (0,)):
+        say(f"[case] probe B={B} d_model={d_model} Hq={Hq} d={d} {dtype} path={path}")
+        with pb.options(probe=path):
+            rho = pb.probe(W, x, wl.Hq, wl.d)
+        torch.cuda.synchronize()
+        e = rel_l2(to64(rho), want)
+        say(f"probe B={B} d_model={d_model} path={path}: rel {e:.3e}")
+        assert e <= RHO_REL_L2
