@@ -355,3 +355,54 @@ def test_probe_shapes(B, d_model, dtype, Hq, d):
         e = rel_l2(to64(rho), want)
         say(f"probe B={B} d_model={d_model} path={path}: rel {e:.3e}")
         assert e <= RHO_REL_L2
+
+
+def test_cache_past_4gib():
+    """K and V of 5.2 GB each, so the streams of the later sequences start past
+    byte 2^32: the ragged workload's shapes over a 40000-key cache (lengths
+    log-uniform in [128, 40000], the last sequence full, K/V drawn on the
+    device), through the automatic plan (split-K with the compacted item
+    order) and the one-call step. Checked against the oracle on one query
+    head of KV head 7 (the highest stream of its sequence) for every sequence
+    from 40 on and two early ones, plus the first and last head of the
+    longest sequence."""
+    from parallax_covariance_corrected_amd.workloads import device_cache
+    import oracle
+    wl = WORKLOADS[5].scaled(ctx=40000)
+    s = make_inputs(wl, 31, with_kv=False)
+    lens = s.seq_lens.clone()
+    lens[-1] = wl.ctx
+    K, V = device_cache(wl, 32)
+    per_seq = wl.Hkv * wl.ctx * wl.d * 2
+    assert K.numel() * 2 > 2 ** 32 and (wl.B - 1) * per_seq > 2 ** 32
+    say(f"[case] cache past 4 GiB: K, V {K.numel() * 2 / 2 ** 30:.2f} GiB each, "
+        f"lengths {lens.min().item()}..{lens.max().item()}, plan {pb.decode_plan(wl.B, wl.Hq, wl.Hkv, wl.d, wl.ctx)}")
+    G = wl.Hq // wl.Hkv
+    longest = int(torch.argmax(lens))
+    pairs = sorted({(b, 7 * G + b % G) for b in [0, 1] + list(range(40, wl.B))}
+                   | {(longest, 0), (longest, wl.Hq - 1)})
+    W, x, q, dl = s.W_R.cuda(), s.x.cuda(), s.q.cuda(), lens.cuda()
+    rho = pb.probe(W, x, wl.Hq, wl.d)
+    o32 = pb.decode(q, rho, K, V, dl, out_dtype=torch.float32)
+    o16 = pb.decode(q, rho, K, V, dl)
+    step = pb.probe_decode(W, x, q, K, V, dl)
+    torch.cuda.synchronize()
+    assert torch.equal(step.view(torch.int16), o16.view(torch.int16))
+    # host copies of the K/V rows the sampled pairs read
+    need = {}
+    for b, h in pairs:
+        need.setdefault(b, set()).add(h // G)
+    Kp, Vp = {}, {}
+    for b, gs in need.items():
+        n = int(lens[b])
+        Kp[b] = {g: K[b, g, :n].cpu() for g in gs}
+        Vp[b] = {g: V[b, g, :n].cpu() for g in gs}
+    q64 = s.q.float().numpy().astype(np.float64)
+    ref = oracle.decode_heads(q64, oracle_rho(s), Kp, Vp, lens.tolist(), wl.Hkv, pairs)
+    got32 = np.stack([to64(o32[b, h]) for b, h in pairs])
+    got16 = np.stack([to64(o16[b, h]) for b, h in pairs])
+    say(f"past 4 GiB: {len(pairs)} pairs, rel bf16 {rel_l2(got16, ref):.3e}, "
+        f"max-abs fp32 out {max_abs(got32, ref):.3e}")
+    assert np.isfinite(got32).all()
+    assert rel_l2(got16, ref) <= BF16_REL_L2 and max_abs(got32, ref) <= F32OUT_MAX_ABS
+    np.testing.assert_array_equal(got16, bf16_rne(got32))
