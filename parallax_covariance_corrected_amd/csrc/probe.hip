@@ -305,6 +305,13 @@ hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, 
       hipExtLaunchKernelGGL((probe_mfma_kernel<2, 1, 8, 8>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
     } else if (mt == 3) {
       hipExtLaunchKernelGGL((probe_mfma_kernel<3, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
+    } else if ((long long)((N + 31) / 32) * grid.y >= 256) {
+      // 32-column tiles of 16 waves wherever they still make 256 workgroups:
+      // x is read by half as many workgroups (B = 128, 4096 columns: 27.5 ->
+      // 19.4 us; 8192 columns, B = 64: 22.1 -> 15.9 us; with fewer workgroups,
+      // as at B = 64 over 4096 columns, the 16-column tiles stay faster).
+      grid.x = (N + 31) / 32;
+      hipExtLaunchKernelGGL((probe_mfma_kernel<4, 2, 16, 2>), grid, dim3(1024), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
     } else {
       hipExtLaunchKernelGGL((probe_mfma_kernel<4, 1, 8, 4>), grid, dim3(512), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
     }
