@@ -17,6 +17,7 @@
 // where operand reuse across waves pays for staging.
 // fp32 kernel: one wave per output, a plain dot product.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -233,6 +234,126 @@ __global__ __launch_bounds__(kGThreads) void probe_gemm_kernel(const uint16_t* _
     }
 }
 
+// The same 128 x 128 tile product for the common K = 64 * NK, unrolled over K:
+// 64-deep K steps through a four-stage LDS ring (4 x 32 KB), steps k + 1 ..
+// k + 3 in flight while step k is multiplied. Unrolled, every step names its
+// stage and its wait at compile time (in a loop the compiler's tracking of the
+// LDS-destination loads loses the stages at the loop header and waits for all
+// of them). LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r
+// sits at slot c ^ ((r >> 1) & 7), so the 16 rows of one operand read cover
+// the 64 banks once per row pair.
+constexpr int kDK = 64;
+constexpr int kDRow = kDK * 2;
+constexpr int kDPieces = kGM * kDRow / 1024;             // 1 KB pieces per panel
+constexpr int kDLoads = 2 * kDPieces / kGWaves;          // per wave and stage
+static_assert(kDPieces % kGWaves == 0, "every wave loads the same pieces");
+
+__device__ __forceinline__ int deep_slot(int row, int chunk) {
+  return row * kDRow + 16 * (chunk ^ ((row >> 1) & 7));
+}
+
+// Wait until at most N of this wave's vector memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <typename F, int... KT>
+__device__ __forceinline__ void each_step(F& f, std::integer_sequence<int, KT...>) {
+  (f(std::integral_constant<int, KT>{}), ...);
+}
+
+template <int NK>
+__global__ __launch_bounds__(kGThreads) void probe_gemm_deep_kernel(const uint16_t* __restrict__ W,
+                                                                    const uint16_t* __restrict__ x,
+                                                                    float* __restrict__ rho, int B,
+                                                                    int N) {
+  constexpr int K = NK * kDK;
+  __shared__ __attribute__((aligned(16))) unsigned char sA0[kGM * kDRow], sA1[kGM * kDRow],
+      sA2[kGM * kDRow], sA3[kGM * kDRow];
+  __shared__ __attribute__((aligned(16))) unsigned char sB0[kGN * kDRow], sB1[kGN * kDRow],
+      sB2[kGN * kDRow], sB3[kGN * kDRow];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int wm = wave / kGWN, wn = wave % kGWN;
+  const int m0 = blockIdx.y * kGM, n0 = blockIdx.x * kGN;
+  constexpr unsigned rowb = (unsigned)K * 2;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (size_t)m0 * K, (unsigned)min(B - m0, kGM) * rowb);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + (size_t)n0 * K, (unsigned)min(N - n0, kGN) * rowb);
+
+  auto stage = [&](auto KT) {
+    constexpr int kt = decltype(KT)::value, st = kt % 4;
+    unsigned char* a = st == 0 ? sA0 : st == 1 ? sA1 : st == 2 ? sA2 : sA3;
+    unsigned char* b = st == 0 ? sB0 : st == 1 ? sB1 : st == 2 ? sB2 : sB3;
+#pragma unroll
+    for (int pc = 0; pc < kDPieces / kGWaves; ++pc) {
+      const int piece = pc * kGWaves + wave;
+      const int byte = piece * 1024 + 16 * lane;
+      const int row = byte / kDRow, sc = (byte % kDRow) / 16;
+      const unsigned off = (unsigned)row * rowb + (unsigned)(kt * kDK + 8 * (sc ^ ((row >> 1) & 7))) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)&a[piece * 1024], 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)&b[piece * 1024], 16, off, 0, 0, 0);
+    }
+  };
+
+  f32x4 acc[kGTI][kGTJ];
+#pragma unroll
+  for (int i = 0; i < kGTI; ++i)
+#pragma unroll
+    for (int jn = 0; jn < kGTJ; ++jn) acc[i][jn] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](auto KT) {
+    constexpr int kt = decltype(KT)::value, st = kt % 4;
+    const unsigned char* a = st == 0 ? sA0 : st == 1 ? sA1 : st == 2 ? sA2 : sA3;
+    const unsigned char* b = st == 0 ? sB0 : st == 1 ? sB1 : st == 2 ? sB2 : sB3;
+    // this wave's loads of step kt done (those of kt + 1, kt + 2 may not be)
+    wait_vm<(kt + 2 < NK ? 2 : kt + 1 < NK ? 1 : 0) * kDLoads>();
+    // A bare barrier: __syncthreads() would also wait for the later stages'
+    // loads. After it every wave's part of stage kt is in LDS, and every wave
+    // has finished reading the stage of step kt - 1, which step kt + 3 reuses.
+    // The empty asm statements keep the compiler from moving memory accesses
+    // across the barrier.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if constexpr (kt + 3 < NK) stage(std::integral_constant<int, kt + 3>{});
+#pragma unroll
+    for (int ks = 0; ks < kDK / 32; ++ks) {
+      u32x4 av[kGTI], bv[kGTJ];
+#pragma unroll
+      for (int i = 0; i < kGTI; ++i)
+        av[i] = *(const u32x4*)&a[deep_slot(wm * 16 * kGTI + 16 * i + l16, 4 * ks + grp)];
+#pragma unroll
+      for (int jn = 0; jn < kGTJ; ++jn)
+        bv[jn] = *(const u32x4*)&b[deep_slot(wn * 16 * kGTJ + 16 * jn + l16, 4 * ks + grp)];
+#pragma unroll
+      for (int i = 0; i < kGTI; ++i)
+#pragma unroll
+        for (int jn = 0; jn < kGTJ; ++jn)
+          acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i]), as_bf16x8(bv[jn]),
+                                                                acc[i][jn], 0, 0, 0);
+    }
+  };
+  stage(std::integral_constant<int, 0>{});
+  if constexpr (NK > 1) stage(std::integral_constant<int, 1>{});
+  if constexpr (NK > 2) stage(std::integral_constant<int, 2>{});
+  each_step(step, std::make_integer_sequence<int, NK>{});
+
+#pragma unroll
+  for (int i = 0; i < kGTI; ++i)
+#pragma unroll
+    for (int jn = 0; jn < kGTJ; ++jn) {
+      const int col = n0 + wn * 16 * kGTJ + 16 * jn + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * 16 * kGTI + 16 * i + 4 * grp + r;
+        if (row < B && col < N) store_stream(rho + (size_t)row * N + col, acc[i][jn][r]);
+      }
+    }
+}
+
 // fp32: one wave per output rho[row][col]; lane l takes elements l, l + 64, ...
 // of the dot product (each load instruction reads 256 contiguous bytes of the
 // W_R row and of x), four accumulators, then a wave sum.
@@ -284,6 +405,20 @@ hipError_t launch_probe(const void* W, const void* x, float* rho, int B, int N, 
   if (gemm) {
     dim3 grid((N + kGN - 1) / kGN, (B + kGM - 1) / kGM);
     if (grid.y > 65535u) return hipErrorInvalidConfiguration;
+#define PARALLAX_DEEP(NK)                                                                   \
+  case NK * kDK:                                                                            \
+    hipExtLaunchKernelGGL(probe_gemm_deep_kernel<NK>, grid, dim3(kGThreads), 0, s, ev.start, \
+                          ev.stop, 0, Wb, xb, rho, B, N);                                   \
+    return hipGetLastError();
+    switch (K) {
+      PARALLAX_DEEP(16)
+      PARALLAX_DEEP(32)
+      PARALLAX_DEEP(40)
+      PARALLAX_DEEP(48)
+      PARALLAX_DEEP(64)
+      default: break;
+    }
+#undef PARALLAX_DEEP
     hipExtLaunchKernelGGL(probe_gemm_kernel, grid, dim3(kGThreads), 0, s, ev.start, ev.stop, 0, Wb, xb, rho, B, N, K);
   } else {
     // Shapes picked by a sweep over cold W_R (tiles of 8 / 16 columns, 4-16
