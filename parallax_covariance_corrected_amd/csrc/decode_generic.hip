@@ -92,63 +92,88 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(PARALLAX_DECODE_HEA
   const int kg = lane / LPK, sub = lane % LPK;
   const int h0 = kvh * G + hb * GB;
 
-  const float* rsrc = a.rho;   // null: softmax only
-  if constexpr (FUSED) {
-    __shared__ float sR[GB * D];
-    probe_rows<F32IN, 256>(a.W_R, (const char*)a.x + (size_t)b * a.d_model * E::kSize, a.d_model,
-                           (size_t)h0 * D, GB * D, sR);
-    __syncthreads();
-    rsrc = sR;
-  }
-  float qf[GB][EPL], rf[GB][EPL];
-#pragma unroll
-  for (int h = 0; h < GB; ++h) {
-    const size_t base = ((size_t)b * a.Hq + h0 + h) * D + sub * EPL;
-    const u32x4 qw = *(const u32x4*)((const char*)a.q + base * E::kSize);
-    E::unpack(qw, qf[h]);
-    const size_t rbase = FUSED ? (size_t)h * D + sub * EPL : base;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) rf[h][i] = rsrc ? rsrc[rbase + i] : 0.f;
-  }
-
-  float m[GB], l[GB], S[GB], A[GB][EPL], P[GB][EPL];
-#pragma unroll
-  for (int h = 0; h < GB; ++h) {
-    m[h] = kNegInf; l[h] = 0.f; S[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) { A[h][i] = 0.f; P[h][i] = 0.f; }
-  }
-
+  // Keys are taken in batches of U per lane whose K/V loads are in flight
+  // together; the first batch and q are requested before the probe, so that
+  // their memory round trips overlap the probe's.
+  constexpr int U = 4;
+  constexpr int STEP = 4 * KPW;      // keys between a lane's consecutive keys
   const size_t seq = ((size_t)cb * a.Hkv + kvh) * (size_t)a.max_ctx;
   const char* kb = (const char*)a.k + seq * ROW + sub * 16;
   const char* vb = (const char*)a.v + seq * ROW + sub * 16;
+  u32x4 kw[U], vw[U];
+  auto fetch = [&](int jb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = jb + u * STEP;
+        kw[u] = j < c1 ? *(const u32x4*)(kb + (size_t)j * ROW) : (u32x4){0u, 0u, 0u, 0u};
+        vw[u] = j < c1 ? *(const u32x4*)(vb + (size_t)j * ROW) : (u32x4){0u, 0u, 0u, 0u};
+      }
+    };
+    const int j0 = c0 + wave * KPW + kg;
+    u32x4 qw[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h)
+      qw[h] = *(const u32x4*)((const char*)a.q + (((size_t)b * a.Hq + h0 + h) * D + sub * EPL) * E::kSize);
+    fetch(j0);
 
-  for (int j = c0 + wave * KPW + kg; j < c1; j += 4 * KPW) {
-    const u32x4 kw = *(const u32x4*)(kb + (size_t)j * ROW);
-    const u32x4 vw = *(const u32x4*)(vb + (size_t)j * ROW);
-    float kf[EPL], vf[EPL];
-    E::unpack(kw, kf);
-    E::unpack(vw, vf);
+    const float* rsrc = a.rho;   // null: softmax only
+    if constexpr (FUSED) {
+      __shared__ float sR[GB * D];
+      probe_rows<F32IN, 256>(a.W_R, (const char*)a.x + (size_t)b * a.d_model * E::kSize, a.d_model,
+                             (size_t)h0 * D, GB * D, sR);
+      __syncthreads();
+      rsrc = sR;
+    }
+    float qf[GB][EPL], rf[GB][EPL];
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
-      float s = 0.f, p = 0.f;
+      E::unpack(qw[h], qf[h]);
+      const size_t rbase = FUSED ? (size_t)h * D + sub * EPL : ((size_t)b * a.Hq + h0 + h) * D + sub * EPL;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) { s = fmaf(qf[h][i], kf[i], s); p = fmaf(rf[h][i], kf[i], p); }
+      for (int i = 0; i < EPL; ++i) rf[h][i] = rsrc ? rsrc[rbase + i] : 0.f;
+    }
+
+    float m[GB], l[GB], S[GB], A[GB][EPL], P[GB][EPL];
 #pragma unroll
-      for (int o = 1; o < LPK; o <<= 1) { s += __shfl_xor(s, o); p += __shfl_xor(p, o); }
-      s *= a.scale_log2;
-      const float mn = fmaxf(m[h], s);
-      const float al = rescale(m[h], mn);
-      const float e = fast_exp2(s - mn);
-      const float ep = e * p;
-      l[h] = fmaf(l[h], al, e);
-      S[h] = fmaf(S[h], al, ep);
+    for (int h = 0; h < GB; ++h) {
+      m[h] = kNegInf; l[h] = 0.f; S[h] = 0.f;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        A[h][i] = fmaf(A[h][i], al, e * vf[i]);
-        P[h][i] = fmaf(P[h][i], al, ep * vf[i]);
+      for (int i = 0; i < EPL; ++i) { A[h][i] = 0.f; P[h][i] = 0.f; }
+    }
+
+    for (int jb = j0; jb < c1; jb += U * STEP) {
+      u32x4 kc[U], vc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) { kc[u] = kw[u]; vc[u] = vw[u]; }
+      if (jb + U * STEP < c1) fetch(jb + U * STEP);   // the next batch in flight
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+      const int j = jb + u * STEP;
+      if (j >= c1) break;
+      float kf[EPL], vf[EPL];
+      E::unpack(kc[u], kf);
+      E::unpack(vc[u], vf);
+#pragma unroll
+      for (int h = 0; h < GB; ++h) {
+        float s = 0.f, p = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) { s = fmaf(qf[h][i], kf[i], s); p = fmaf(rf[h][i], kf[i], p); }
+#pragma unroll
+        for (int o = 1; o < LPK; o <<= 1) { s += __shfl_xor(s, o); p += __shfl_xor(p, o); }
+        s *= a.scale_log2;
+        const float mn = fmaxf(m[h], s);
+        const float al = rescale(m[h], mn);
+        const float e = fast_exp2(s - mn);
+        const float ep = e * p;
+        l[h] = fmaf(l[h], al, e);
+        S[h] = fmaf(S[h], al, ep);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          A[h][i] = fmaf(A[h][i], al, e * vf[i]);
+          P[h][i] = fmaf(P[h][i], al, ep * vf[i]);
+        }
+        m[h] = mn;
       }
-      m[h] = mn;
     }
   }
 
