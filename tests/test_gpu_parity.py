@@ -407,3 +407,36 @@ def test_cache_past_4gib():
     assert np.isfinite(got32).all()
     assert rel_l2(got16, ref) <= BF16_REL_L2 and max_abs(got32, ref) <= F32OUT_MAX_ABS
     np.testing.assert_array_equal(got16, bf16_rne(got32))
+
+
+@pytest.mark.parametrize("opts", [{}, {"chunk": 128}, {"kernel": 1}])
+def test_zero_covariance_closed_forms(opts):
+    """Degenerate covariance against closed forms, not the oracle: all keys of a
+    sequence equal (equal scores, uniform weights, C = 0) gives the mean of its
+    values; all values equal gives that value, whatever rho. The probe is made
+    large (W_R ~ N(0, 1)), so the one-pass form's P/l - vbar S/l must cancel to
+    within fp32 rounding of |p| |vbar|."""
+    wl = WORKLOADS[2].scaled(B=3, Hq=8, Hkv=2, ctx=700, d_model=64, wr_std=1.0)
+    s = make_inputs(wl, 41, lengths=[700, 513, 300])
+    K0, V1 = s.K[0].clone(), s.V[1].clone()
+    K0[:] = K0[:, :1, :]                # sequence 0: every key equal to its first
+    V1[:] = V1[:, :1, :]                # sequence 1: every value equal to its first
+    s.K[0], s.V[1] = K0, V1
+    say(f"[case] zero covariance {opts}")
+    dev = Device(s)
+    rho = dev.probe()
+    with pb.options(**opts):
+        o32 = to64(dev.decode(rho, out_dtype=torch.float32))
+        o16 = to64(dev.decode(rho))
+    torch.cuda.synchronize()
+    G = wl.Hq // wl.Hkv
+    want0 = np.stack([s.V[0][h // G][:700].double().numpy().mean(0) for h in range(wl.Hq)])
+    want1 = np.stack([s.V[1][h // G][0].double().numpy() for h in range(wl.Hq)])
+    p_scale = float(np.abs(to64(rho)).sum(-1).max()) * float(np.abs(s.K[0][0][0].double().numpy()).max())
+    err0, err1 = max_abs(o32[0], want0), max_abs(o32[1], want1)
+    say(f"zero covariance {opts}: max-abs equal keys {err0:.2e}, equal values {err1:.2e}, |p| scale {p_scale:.1f}")
+    assert err0 <= 1e-6 * max(p_scale, 1.0) + 1e-5 and err1 <= 1e-6 * max(p_scale, 1.0) + 1e-5
+    np.testing.assert_array_equal(o16, bf16_rne(o32))
+    # sequence 2 is untouched: ordinary parity
+    ref2 = oracle_out(s, oracle_rho(s), [(2, h) for h in range(wl.Hq)])
+    assert max_abs(o32[2], ref2) <= F32OUT_MAX_ABS
