@@ -340,7 +340,8 @@ def test_workspace_grows_across_shapes_and_streams():
     (2048, 2048, "bf16", 16, 128), (300, 520, "bf16", 3, 64), (129, 4096, "bf16", 5, 128),
     (40, 2048, "bf16", 16, 128), (48, 1024, "bf16", 32, 128), (33, 264, "bf16", 5, 64),
     (128, 2560, "bf16", 32, 128), (97, 264, "bf16", 6, 64), (64, 2048, "bf16", 64, 128),
-    (120, 520, "bf16", 66, 64), (70, 3072, "bf16", 4, 128)])
+    (120, 520, "bf16", 66, 64), (70, 3072, "bf16", 4, 128), (200, 1024, "bf16", 3, 64),
+    (257, 2560, "bf16", 7, 128)])
 def test_probe_shapes(B, d_model, dtype, Hq, d):
     """Automatic kernel choice, then (bf16) each of the two probe kernels forced:
     the small-batch kernel in row blocks and the tiled GEMM, at every batch."""
