@@ -11,10 +11,12 @@ its K/V cold (their total exceeds the last-level cache).
 Output: one JSON line (metric, value = decode tokens/s, ms_per_step, roofline
 of the dominant kernel, CPU oracle baseline, ...), with a compact record per
 other workload under "configs" (step and per-kernel times, algorithmic bytes,
-fraction of peak, launch plan).
+fraction of peak, launch plan) and a compact batch x context record under
+"sweep" (--sweep runs the whole grid, one line per point).
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload 2]
-                    [--sets 3] [--no-cpu-baseline] [--no-configs] [--sweep] [--fusion-sweep]
+                    [--sets 3] [--no-cpu-baseline] [--no-configs] [--no-sweep-record]
+                    [--sweep] [--fusion-sweep]
                     [--copy-calibration]
 """
 from __future__ import annotations
@@ -448,97 +450,125 @@ def run_workload(args, wl_id: int, emit: bool = True):
         torch.cuda.empty_cache()
         rec["configs"] = {str(i): run_config(args, i, max(args.steps, 20))
                           for i in sorted(WORKLOADS) if i != wl_id}
+    if args.configs and args.sweep_record:
+        rec["sweep"] = compact_sweep(pb)
     if emit:
         print(json.dumps(rec), flush=True)
     return rec
 
 
-def run_sweep(args):
-    """Batch x context sweep at Hq=16, Hkv=8, d=128, d_model=2048, bf16. Per point,
-    on rotated K/V sets (so that every call reads cold data): the decode call
-    (split-K pass + merge) timed over 100 calls after 20 warm-up calls, each call
-    bracketed by its own events (median, p10, p90), the same calls back to back
-    (mean per call), and the decode kernel's own duration (per-launch events); the probe alone and the whole step through
-    parallax_probe_decode (mean over 100 steps); the share of the correction in
-    the output, ||C rho|| / ||out||. One JSON line per point. GB/s counts K/V,
-    q, rho, out and seq_lens; `pct_peak` is over the decode call's median,
-    `kernel_pct_peak` over the decode kernel's own duration."""
+def sweep_point(pb, B: int, ctx: int, warm: int = 20, reps: int = 100) -> dict:
+    """One batch x context point at Hq=16, Hkv=8, d=128, d_model=2048, bf16, on
+    rotated K/V sets (at least two, three below 768 MB, so that every call
+    reads its K/V cold): the decode call (split-K pass + merge) timed over reps
+    calls after warm warm-up calls, each call bracketed by its own events
+    (median, p10, p90), the same calls back to back (mean per call), the decode
+    kernel's own duration (per-launch events), the probe alone, the whole step
+    through parallax_probe_decode, and the share of the correction in the
+    output, ||C rho|| / ||out||. GB/s counts K/V, q, rho, out and seq_lens;
+    `pct_peak` is over the decode call's median, `kernel_pct_peak` over the
+    decode kernel's own duration."""
     import torch
+    dev, d_model = "cuda", 2048
+    kv = 2 * B * ctx * 8 * 128 * 2
+    nsets = max(2, min(3, (768 << 20) // kv + 1))
+    g = torch.Generator(device=dev).manual_seed(B * 100003 + ctx)
+    sets = []
+    for _ in range(nsets):
+        K = torch.randn((B, 8, ctx, 128), generator=g, device=dev, dtype=torch.bfloat16)
+        V = torch.randn((B, 8, ctx, 128), generator=g, device=dev, dtype=torch.bfloat16)
+        sets.append((K, V))
+    x = torch.randn((B, d_model), generator=g, device=dev).to(torch.bfloat16)
+    W_R = (torch.randn((16 * 128, d_model), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    q = torch.randn((B, 16, 128), generator=g, device=dev).to(torch.bfloat16)
+    rho = pb.probe(W_R, x, 16, 128)
+    lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    out = torch.empty((B, 16, 128), dtype=torch.bfloat16, device=dev)
+
+    def call(i):
+        K, V = sets[i % nsets]
+        pb.decode(q, rho, K, V, lens, out=out)
+
+    for i in range(warm):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        call(i)
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    p10, med, p90 = (t[int(f * (reps - 1))] for f in (0.1, 0.5, 0.9))
+    # the same calls back to back (mean per call), then with per-launch
+    # events: the decode kernel alone
+    b2b = timed_steps(call, reps, warm=5)
+    kus = per_launch_us(pb, call, reps, (("decode", pb.KERNEL_DECODE),))[0]["decode"]
+    pus = per_launch_us(pb, lambda i: pb.probe(W_R, x, 16, 128, out=rho), reps,
+                        (("probe", pb.KERNEL_PROBE),))[0]["probe"]
+
+    def step(i):
+        K, V = sets[i % nsets]
+        pb.probe_decode(W_R, x, q, K, V, lens, out=out)
+
+    step_us = timed_steps(step, reps, warm=5)
+    par = pb.decode(q, rho, *sets[0], lens, out_dtype=torch.float32)
+    soft = pb.softmax_decode(q, *sets[0], lens, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    corr = float((par - soft).norm() / par.norm())
+    byts = kv + B * 16 * 128 * (2 + 4 + 2) + B * 4
+    chunk, splits, kern = pb.decode_plan(B, 16, 8, 128, ctx)
+    del sets, q, rho, lens, out, x, W_R, par, soft
+    torch.cuda.empty_cache()
+
+    def pct(us):
+        return round(100 * byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)
+    return {"B": B, "ctx": ctx, "plan": [chunk, splits, kern],
+            "us_per_step": round(med, 2), "p10_us": round(p10, 2),
+            "p90_us": round(p90, 2),
+            "tokens_per_s": round(B / (med * 1e-6), 1),
+            "gbps": round(byts / (med * 1e-6) / 1e9, 1),
+            "pct_peak": pct(med),
+            "call_us_back_to_back": round(b2b, 2), "call_pct_peak_back_to_back": pct(b2b),
+            "kernel_us": round(kus, 2), "kernel_pct_peak": pct(kus),
+            "probe_us": round(pus, 2), "probe_decode_step_us": round(step_us, 2),
+            "correction_to_output": round(corr, 4)}
+
+
+def run_sweep(args):
+    """Batch x context sweep (B 1..2048, ctx 128..32768, powers of two): one JSON
+    line per point (sweep_point)."""
     from parallax_covariance_corrected_amd import binding as pb
     from parallax_covariance_corrected_amd.workloads import sweep_points
 
-    dev = "cuda"
-    warm, reps, d_model = 20, 100, 2048
     max_bytes = args.sweep_max_gib << 30
     for (B, ctx) in sweep_points(max_bytes // 2 if args.sweep_max_gib else 64 << 30):
-        kv = 2 * B * ctx * 8 * 128 * 2
-        # At least two sets (three below 768 MB) alternate, so that between two
-        # calls on one set at least 768 MB of other K/V streams through the
-        # 256 MB last-level cache: every call reads its K/V cold.
-        nsets = max(2, min(3, (768 << 20) // kv + 1))
-        g = torch.Generator(device=dev).manual_seed(B * 100003 + ctx)
-        sets = []
-        for _ in range(nsets):
-            K = torch.randn((B, 8, ctx, 128), generator=g, device=dev, dtype=torch.bfloat16)
-            V = torch.randn((B, 8, ctx, 128), generator=g, device=dev, dtype=torch.bfloat16)
-            sets.append((K, V))
-        x = torch.randn((B, d_model), generator=g, device=dev).to(torch.bfloat16)
-        W_R = (torch.randn((16 * 128, d_model), generator=g, device=dev) * 0.02).to(torch.bfloat16)
-        q = torch.randn((B, 16, 128), generator=g, device=dev).to(torch.bfloat16)
-        rho = pb.probe(W_R, x, 16, 128)
-        lens = torch.full((B,), ctx, dtype=torch.int32, device=dev)
-        out = torch.empty((B, 16, 128), dtype=torch.bfloat16, device=dev)
+        print(json.dumps({"sweep": True, **sweep_point(pb, B, ctx)}), flush=True)
 
-        def call(i):
-            K, V = sets[i % nsets]
-            pb.decode(q, rho, K, V, lens, out=out)
 
-        for i in range(warm):
-            call(i)
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
-        for i, (a, b) in enumerate(ev):
-            a.record()
-            call(i)
-            b.record()
-        torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-        p10, med, p90 = (t[int(f * (reps - 1))] for f in (0.1, 0.5, 0.9))
-        # the same calls back to back (mean per call), then with per-launch
-        # events: the decode kernel alone
-        b2b = timed_steps(call, reps, warm=5)
-        kus = per_launch_us(pb, call, reps, (("decode", pb.KERNEL_DECODE),))[0]["decode"]
-        pus = per_launch_us(pb, lambda i: pb.probe(W_R, x, 16, 128, out=rho), reps,
-                            (("probe", pb.KERNEL_PROBE),))[0]["probe"]
+# Points of the compact sweep record in the default line: batch 1 .. 512 by
+# factors of 8 against a short, a mid and a long context (K+V up to 16 GiB).
+COMPACT_SWEEP = [(B, c) for B in (1, 8, 64, 512) for c in (256, 4096, 32768)
+                 if 2 * B * c * 8 * 128 * 2 <= 16 << 30]
 
-        def step(i):
-            K, V = sets[i % nsets]
-            pb.probe_decode(W_R, x, q, K, V, lens, out=out)
 
-        step_us = timed_steps(step, reps, warm=5)
-        par = pb.decode(q, rho, *sets[0], lens, out_dtype=torch.float32)
-        soft = pb.softmax_decode(q, *sets[0], lens, out_dtype=torch.float32)
-        torch.cuda.synchronize()
-        corr = float((par - soft).norm() / par.norm())
-        byts = kv + B * 16 * 128 * (2 + 4 + 2) + B * 4
-        chunk, splits, kern = pb.decode_plan(B, 16, 8, 128, ctx)
-
-        def pct(us):
-            return round(100 * byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)
-        print(json.dumps({"sweep": True, "B": B, "ctx": ctx, "plan": [chunk, splits, kern],
-                          "us_per_step": round(med, 2), "p10_us": round(p10, 2),
-                          "p90_us": round(p90, 2),
-                          "tokens_per_s": round(B / (med * 1e-6), 1),
-                          "gbps": round(byts / (med * 1e-6) / 1e9, 1),
-                          "pct_peak": pct(med),
-                          "call_us_back_to_back": round(b2b, 2), "call_pct_peak_back_to_back": pct(b2b),
-                          "kernel_us": round(kus, 2), "kernel_pct_peak": pct(kus),
-                          "probe_us": round(pus, 2), "probe_decode_step_us": round(step_us, 2),
-                          "correction_to_output": round(corr, 4)}),
-              flush=True)
-        del sets, q, rho, lens, out, x, W_R, par, soft
-        torch.cuda.empty_cache()
+def compact_sweep(pb) -> dict:
+    """A subset of the batch x context sweep for the default line: per point
+    the decode kernel's and the decode call's fraction of peak, the one-call
+    step and its tokens/s (50 calls per measurement)."""
+    pts = []
+    for (B, c) in COMPACT_SWEEP:
+        print(f"# bench: sweep point B={B} ctx={c}", file=sys.stderr, flush=True)
+        r = sweep_point(pb, B, c, warm=10, reps=50)
+        pts.append({"B": B, "ctx": c, "plan": r["plan"], "kernel_us": r["kernel_us"],
+                    "kernel_pct_peak": r["kernel_pct_peak"],
+                    "call_us_back_to_back": r["call_us_back_to_back"],
+                    "call_pct_peak_back_to_back": r["call_pct_peak_back_to_back"],
+                    "step_us": r["probe_decode_step_us"],
+                    "step_tokens_per_s": round(B / (r["probe_decode_step_us"] * 1e-6), 1)})
+    return {"model": "Hq 16, Hkv 8, d 128, d_model 2048, bf16, every sequence full",
+            "points": pts}
 
 
 def run_fusion_sweep(args):
@@ -694,6 +724,8 @@ def main():
     ap.add_argument("--no-configs", dest="configs", action="store_false",
                     help="skip the compact records of the other four workloads")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--no-sweep-record", dest="sweep_record", action="store_false",
+                    help="skip the compact batch x context record of the default line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 256 MiB device-to-device 3 times (a kernel of known "
                          "traffic, to scale hardware byte counters)")
