@@ -177,3 +177,49 @@ def test_prefill_rejects_bad_arguments():
         pb.prefill(q, rho, K[:, :, :4].contiguous(), K[:, :, :4].contiguous())   # T > max_ctx
     with pytest.raises(ValueError):
         pb.prefill(q, rho, K.float(), K.float())      # mixed dtypes
+
+
+def test_prefill_zero_covariance_closed_forms():
+    """The causal forward on degenerate caches, against closed forms: all keys
+    of sequence 0 equal (token t sees prefix + t + 1 equal scores, so its output
+    is the mean of those values) and all values of sequence 1 equal (every
+    output is that value), with a large probe (W_R ~ N(0, 1), |p| up to a few
+    hundred) so that the one-pass form must cancel P/l - vbar S/l; sequence 2
+    is ordinary. The bound per output row follows the kernel's precision
+    model: e p enters the matrix cores as a 16-bit hi + lo pair while S sums it
+    in fp32, so the cancellation leaves at most 2^-16 sum_j w_j |p_j| |v_j|
+    (w, p in fp64 from the same inputs), plus fp32 rounding."""
+    wl = WORKLOADS[2].scaled(B=3, Hq=8, Hkv=2, d=128, d_model=64, wr_std=1.0)
+    prefix = [40, 0, 17]
+    s = make_prefill_inputs(wl, 150, prefix, seed=77)
+    K0, V1 = s.K[0].clone(), s.V[1].clone()
+    K0[:] = K0[:, :1, :]
+    V1[:] = V1[:, :1, :]
+    s.K[0], s.V[1] = K0, V1
+    say("[case] prefill zero covariance")
+    rho = _rho(s)
+    o32 = _run(s, rho, torch.float32)
+    obf = _run(s, rho, torch.bfloat16)
+    G = wl.Hq // wl.Hkv
+    q64 = s.q.float().numpy().astype(np.float64)
+    r64 = rho.astype(np.float64)
+    worst = 0.0
+    for b, closed in ((0, "mean"), (1, "value")):
+        for g in range(wl.Hkv):
+            Kg, Vg = s.K[b][g].double().numpy(), s.V[b][g].double().numpy()
+            for t in range(s.T):
+                n = prefix[b] + t + 1
+                want = Vg[:n].mean(0) if closed == "mean" else Vg[0]
+                for h in range(g * G, (g + 1) * G):
+                    w = oracle.softmax_weights(q64[b, t, h], Kg[:n])
+                    p = np.abs(Kg[:n] @ r64[b, t, h])
+                    bound = 2.0 ** -16 * float(w @ (p * np.abs(Vg[:n]).max(1))) + 2e-6
+                    err = float(np.abs(o32[b, t, h] - want).max())
+                    worst = max(worst, err / bound)
+                    assert err <= bound, (b, t, h, err, bound)
+    say(f"prefill zero covariance: worst error / model bound {worst:.3f}")
+    np.testing.assert_array_equal(obf, bf16_rne(o32))
+    rows = [(2, t, h) for t in (0, 75, 149) for h in range(wl.Hq)]
+    ref = oracle.prefill_rows(s.q, r64, s.K, s.V, s.prefix.numpy(), wl.Hkv, rows)
+    got = np.stack([o32[b, t, h] for b, t, h in rows])
+    assert rel_l2(got, ref) <= F32OUT_REL
